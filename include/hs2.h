@@ -1,0 +1,179 @@
+/*
+ * hs2.h -- C ABI of the HySparse2 attention hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, with one KV head shared by 64 query heads (MQA):
+ *   hs2_bridge_kv         KV Bridging: one read of the self-decoder hidden states is
+ *                         projected through separate K/V weights for several layers.
+ *   hs2_full_attn_select  the cross-decoder full-attention (selector) layer: exact
+ *                         causal attention, plus, for each query, the top_k keys outside
+ *                         the forced window ranked by their softmax probability summed
+ *                         over the query heads.
+ *   hs2_sparse_attn       a sparse layer of the same hybrid block: attention over the
+ *                         forced window plus the selector's rows only, on the selector's
+ *                         KV cache.
+ *
+ * Sources (page title and section; the pages are news and commentary on the HySparse2
+ * paper):
+ *   [arex]     arex-research.com, "Xiaomi MiMo lead Luo Fuli publishes the MiMo-V3 core
+ *              architecture HySparse2", sections "Outer KV Bridging, inner KV Reuse" and
+ *              "Numbers computed on three 80B-A3B models".
+ *   [toolnavs] toolnavs.com (German) article on the core architecture of Xiaomi MiMo-V3,
+ *              section "Was HySparse2 tut".
+ *   [zgeo]     zgeo.com.cn, "Xiaomi HySparse2 architecture deep dive", section
+ *              "Core technical principles".
+ *
+ * Conventions shared by every call
+ *   - All tensors are row-major, contiguous and 16-byte aligned device memory unless a
+ *     parameter says "host".
+ *   - Q:   [total_q][n_heads][head_dim]          (query rows of one layer)
+ *   - K,V: [total_kv_rows][head_dim]             (one KV head; sequences packed)
+ *   - Positions are sequence-local: row kv_start[s] + j holds position j of sequence s.
+ *   - The window of query position t is the `window` most recent positions including t:
+ *     rows max(0, t-window+1) .. t. Candidates for selection are rows 0 .. t-window.
+ *   - Selected indices are sequence-local candidate positions, ascending, padded with -1.
+ *   - LSE outputs are natural-log log-sum-exp of the scaled logits, fp32.
+ *   - The caller owns every buffer and the stream. The library allocates nothing, keeps
+ *     no state between calls and never synchronises the stream. Inputs are read-only;
+ *     outputs and the workspace must not alias any input or each other.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and the call
+ *     returns; device faults surface at the caller's next synchronisation.
+ *   - Argument checks run on the host before anything is enqueued. A failing check
+ *     returns a negative hs2_status, enqueues nothing and sets hs2_last_error().
+ *     A failing launch returns HS2_ERR_HIP.
+ *   - Device-side descriptor values are not read by the host. A query whose descriptor
+ *     is inconsistent (q_pos outside [0, kv_len), rows outside [0, total_kv_rows))
+ *     is not computed: its outputs are NaN and its sel_count is -1. No memory outside
+ *     the given buffers is touched.
+ *   - Supported shapes: n_heads == 64, head_dim == 128 (the MQA layout of the pages,
+ *     [arex] "Numbers computed on three 80B-A3B models"); anything else returns
+ *     HS2_ERR_UNSUPPORTED. 1 <= window <= 1<<20, 0 <= top_k <= HS2_MAX_TOP_K.
+ *   - Sequence lengths up to 2^31-1 rows; total rows up to 2^62.
+ */
+#ifndef HS2_H_
+#define HS2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS2_VERSION 10000 /* 1.0.0 */
+#define HS2_MAX_TOP_K 4096
+
+typedef enum hs2_status {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARG = -1, /* a null pointer, a negative size, inconsistent sizes     */
+  HS2_ERR_UNSUPPORTED = -2, /* a valid but unsupported shape or dtype                  */
+  HS2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the size query says   */
+  HS2_ERR_HIP = -4          /* the HIP runtime reported an error while enqueueing      */
+} hs2_status;
+
+typedef enum hs2_dtype {
+  HS2_BF16 = 0, /* bfloat16 storage, fp32 arithmetic (bf16 MFMA with fp32 accumulation) */
+  HS2_F32 = 1   /* float32 storage and arithmetic                                      */
+} hs2_dtype;
+
+/* A ragged batch of sequences and their queries. */
+typedef struct hs2_seqs {
+  int32_t num_seqs;        /* host: number of sequences, >= 1                               */
+  const int64_t* kv_start; /* device [num_seqs]: first row of sequence s in K and V         */
+  const int32_t* kv_len;   /* device [num_seqs]: n_s, cached rows of s (current token incl.)*/
+  const int32_t* q_start;  /* device [num_seqs+1]: queries of s are rows q_start[s] ..
+                              q_start[s+1]-1 of Q; q_start[0] == 0, non-decreasing          */
+  const int32_t* q_pos;    /* device [total_q]: position t of each query, 0 <= t < n_s      */
+  int32_t total_q;         /* host: q_start[num_seqs]                                      */
+  int32_t max_kv_len;      /* host: an upper bound of every kv_len                         */
+  int64_t total_kv_rows;   /* host: rows of K and V                                        */
+  int32_t max_q_per_seq;   /* host: an upper bound of the queries of any one sequence      */
+} hs2_seqs;
+
+/* Library version: HS2_VERSION of the built library. */
+int32_t hs2_version(void);
+
+/* Text of the last failed check on the calling thread; "" if none. Valid until the
+ * next call on the same thread. */
+const char* hs2_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * KV Bridging ([arex] "Outer KV Bridging, inner KV Reuse"; [toolnavs] "Was HySparse2
+ * tut"): every cross-decoder full-attention layer l builds its own K and V from the
+ * input hidden states H of the matching self-decoder full-attention layer, through its
+ * own projections, and one source may feed several layers:
+ *     K_l = H W_K^l,   V_l = H W_V^l,   l = 0 .. n_layers-1
+ * Plain linear maps: no bias, normalisation or rotary embedding is applied.
+ *
+ *   hidden   device [n_rows][d_model], bf16
+ *   w_k,w_v  HOST arrays of n_layers DEVICE pointers, each [d_model][head_dim] bf16
+ *   k_out,   HOST arrays of n_layers DEVICE pointers, each [n_rows][head_dim] bf16,
+ *   v_out    written with round-to-nearest-even from fp32 accumulation
+ *   Limits: dt == HS2_BF16; head_dim == 128; d_model a multiple of 64, <= 65536;
+ *           1 <= n_layers <= 8; n_rows >= 0 (0 enqueues nothing).
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t head_dim);
+
+hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                         const void* const* w_k, const void* const* w_v, void* const* k_out,
+                         void* const* v_out, int32_t head_dim, void* workspace,
+                         size_t workspace_bytes, hs2_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Full-attention selector layer ([arex] "Outer KV Bridging, inner KV Reuse": the few
+ * full-attention layers act as the indexer, with their exact attention scores;
+ * [toolnavs] "Was HySparse2 tut"). For each query i at position t of sequence s:
+ *     s_hj  = scale * <q_h, k_j>,  j = 0..t           (all 64 heads share k_j, v_j)
+ *     out_h = sum_j softmax_j(s_h) v_j,  lse_h = log sum_j exp(s_hj)
+ *     score_j = sum_h exp(s_hj - lse_h)  for candidates j = 0..t-window
+ *     sel   = the top_k candidates by score (all of them if fewer), ties to the smaller
+ *             position, written ascending and padded with -1.
+ *
+ *   q        device [total_q][64][128], dtype dt
+ *   k, v     device [total_kv_rows][128], dtype dt
+ *   scale    softmax scale, finite and > 0 (1/sqrt(128) for the pages' layout)
+ *   out      device [total_q][64][128], dtype dt
+ *   lse      device [total_q][64] fp32, or NULL
+ *   sel_idx  device [total_q][top_k] int32 (may be NULL when top_k == 0)
+ *   sel_count device [total_q] int32 = min(top_k, candidates), or NULL
+ *   workspace device scratch of at least hs2_full_attn_select_workspace_size(...) bytes,
+ *            256-byte aligned; its contents on entry do not matter.
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_heads,
+                                           int32_t head_dim, int32_t window, int32_t top_k,
+                                           hs2_dtype dt);
+
+hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k,
+                                const void* v, int32_t n_heads, int32_t head_dim,
+                                int32_t window, int32_t top_k, float scale, void* out,
+                                float* lse, int32_t* sel_idx, int32_t* sel_count,
+                                void* workspace, size_t workspace_bytes, hs2_dtype dt,
+                                void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Sparse attention layer with KV Reuse ([arex] "Outer KV Bridging, inner KV Reuse";
+ * [zgeo] "Core technical principles"): a sparse layer reuses the selector's KV cache
+ * and index set; each query attends to its window plus the selected rows only:
+ *     A_t   = {max(0,t-window+1) .. t}  U  {sel_idx[i][r] : 0 <= sel_idx[i][r] <= t-window}
+ *     out_h = sum_{j in A_t} softmax_j(scale * <q_h, k_j>) v_j
+ * Entries of sel_idx outside [0, t-window] (the -1 padding) are ignored. Entries must
+ * be distinct; a repeated entry is counted twice.
+ *
+ *   q        device [total_q][64][128] of this layer, dtype dt
+ *   k, v     the selector's cache, device [total_kv_rows][128]
+ *   sel_idx  device [total_q][top_k] int32 (the selector's output); NULL iff top_k == 0
+ *   out      device [total_q][64][128], dtype dt;  lse device [total_q][64] fp32 or NULL
+ *   workspace as for the selector, sized by hs2_sparse_attn_workspace_size(...)
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim,
+                                      int32_t window, int32_t top_k, hs2_dtype dt);
+
+hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                           const int32_t* sel_idx, int32_t n_heads, int32_t head_dim,
+                           int32_t window, int32_t top_k, float scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* HS2_H_ */

@@ -1,0 +1,395 @@
+// Host entry points of libhs2: argument checks, workspace planning and kernel launches.
+// Every check runs before anything is enqueued; the library allocates nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hs2.h"
+#include "hs2_internal.h"
+
+
+namespace {
+
+using namespace hs2;
+
+thread_local std::string g_err;
+
+hs2_status fail(hs2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hs2_status ok() {
+  g_err.clear();
+  return HS2_OK;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetGroups = 512;  // attention workgroups per launch (2 per CU)
+constexpr int kMaxSplit = 256;      // bound of the split combine
+constexpr int kFilterLen = 16384;   // candidates per top-k filter workgroup
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Split {
+  int n_split;
+  int split_keys;
+};
+
+// Splits the logical key range [0, max_keys) of each query over workgroups so that the
+// launch has about kTargetGroups workgroups; each split is a multiple of 4 waves x 32.
+Split plan_split(int total_q, int64_t max_keys) {
+  const int unit = kTile * kWaves;
+  Split s;
+  if (max_keys <= 0) return Split{1, unit};
+  int want = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(kTargetGroups, std::max(1, total_q))));
+  want = (int)std::min<int64_t>(want, ceil_div(max_keys, unit));
+  s.split_keys = (int)(ceil_div(ceil_div(max_keys, want), unit) * unit);
+  s.n_split = (int)ceil_div(max_keys, s.split_keys);
+  return s;
+}
+
+struct SelectPlan {
+  Split attn, score;
+  int f_split = 1, f_len = kFilterLen;
+  int64_t score_stride = 0;
+  size_t off_part = 0, off_lse2 = 0, off_scores = 0, off_hist = 0, off_counters = 0,
+         off_above = 0, off_cand = 0, total = 0;
+};
+
+SelectPlan plan_select(const hs2_seqs* b, int window, int top_k) {
+  SelectPlan p;
+  const int64_t tq = std::max(0, b->total_q);
+  p.attn = plan_split((int)tq, b->max_kv_len);
+  const int64_t max_cand = std::max<int64_t>(0, (int64_t)b->max_kv_len - window + 1);
+  p.score = plan_split((int)tq, max_cand);
+  p.f_split = (int)std::max<int64_t>(1, ceil_div(max_cand, kFilterLen));
+  p.score_stride = (max_cand + 63) / 64 * 64;
+  size_t off = 0;
+  p.off_part = off;
+  if (p.attn.n_split > 1) off += align_up((size_t)tq * p.attn.n_split * sizeof(Partial));
+  p.off_lse2 = off;
+  off += align_up((size_t)tq * kHeads * sizeof(float));
+  p.off_hist = off;
+  off += align_up((size_t)tq * kHistBins * sizeof(uint32_t));
+  p.off_counters = off;
+  off += align_up((size_t)tq * 4 * sizeof(uint32_t));
+  if (top_k > 0) {
+    p.off_scores = off;
+    off += align_up((size_t)tq * p.score_stride * sizeof(float));
+    p.off_above = off;
+    off += align_up((size_t)tq * top_k * sizeof(int32_t));
+    p.off_cand = off;
+    off += align_up((size_t)tq * kCandCap * sizeof(uint2));
+  }
+  p.total = off;
+  return p;
+}
+
+struct SparsePlan {
+  Split attn;
+  size_t total = 0;
+};
+
+SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k) {
+  SparsePlan p;
+  const int64_t tq = std::max(0, b->total_q);
+  const int64_t max_keys = (int64_t)top_k + std::min<int64_t>(window, b->max_kv_len);
+  p.attn = plan_split((int)tq, max_keys);
+  p.total = p.attn.n_split > 1 ? align_up((size_t)tq * p.attn.n_split * sizeof(Partial)) : 0;
+  return p;
+}
+
+hs2_status check_batch(const hs2_seqs* b) {
+  if (!b) return fail(HS2_ERR_INVALID_ARG, "batch descriptor is NULL");
+  if (b->num_seqs < 1) return fail(HS2_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", b->num_seqs);
+  if (b->total_q < 0) return fail(HS2_ERR_INVALID_ARG, "total_q must be >= 0 (got %d)", b->total_q);
+  if (b->max_kv_len < 1) return fail(HS2_ERR_INVALID_ARG, "max_kv_len must be >= 1 (got %d)", b->max_kv_len);
+  if (b->total_kv_rows < 0) return fail(HS2_ERR_INVALID_ARG, "total_kv_rows must be >= 0");
+  if (b->max_q_per_seq < 0) return fail(HS2_ERR_INVALID_ARG, "max_q_per_seq must be >= 0");
+  if (!b->kv_start || !b->kv_len || !b->q_start || (b->total_q > 0 && !b->q_pos))
+    return fail(HS2_ERR_INVALID_ARG, "batch descriptor has a NULL device array");
+  if (!aligned(b->kv_start, 8) || !aligned(b->kv_len, 4) || !aligned(b->q_start, 4) ||
+      (b->q_pos && !aligned(b->q_pos, 4)))
+    return fail(HS2_ERR_INVALID_ARG, "batch descriptor arrays are misaligned");
+  return HS2_OK;
+}
+
+hs2_status check_attn_common(const hs2_seqs* b, const void* q, const void* k, const void* v,
+                             int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,
+                             float scale, const void* out, const float* lse, hs2_dtype dt) {
+  hs2_status st = check_batch(b);
+  if (st != HS2_OK) return st;
+  if (dt != HS2_BF16 && dt != HS2_F32) return fail(HS2_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dt);
+  if (n_heads != kHeads || head_dim != kDim)
+    return fail(HS2_ERR_UNSUPPORTED, "only n_heads=64, head_dim=128 are supported (got %d, %d)", n_heads,
+                head_dim);
+  if (window < 1 || window > (1 << 20)) return fail(HS2_ERR_INVALID_ARG, "window must be in [1, 2^20] (got %d)", window);
+  if (top_k < 0 || top_k > HS2_MAX_TOP_K)
+    return fail(HS2_ERR_INVALID_ARG, "top_k must be in [0, %d] (got %d)", HS2_MAX_TOP_K, top_k);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(HS2_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (b->total_q > 0 && (!q || !out)) return fail(HS2_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (b->total_kv_rows > 0 && (!k || !v)) return fail(HS2_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(HS2_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(HS2_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (out && (out == q || out == k || out == v)) return fail(HS2_ERR_INVALID_ARG, "out aliases an input");
+  return HS2_OK;
+}
+
+SeqsDev to_dev(const hs2_seqs* b) {
+  SeqsDev d;
+  d.kv_start = b->kv_start;
+  d.kv_len = b->kv_len;
+  d.q_start = b->q_start;
+  d.q_pos = b->q_pos;
+  d.num_seqs = b->num_seqs;
+  d.total_q = b->total_q;
+  d.total_rows = b->total_kv_rows;
+  return d;
+}
+
+hs2_status hip_fail(hipError_t e, const char* what) {
+  return fail(HS2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hs2_version(void) { return HS2_VERSION; }
+
+const char* hs2_last_error(void) { return g_err.c_str(); }
+
+size_t hs2_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim,
+                                           int32_t window, int32_t top_k, hs2_dtype dt) {
+  (void)n_heads;
+  (void)head_dim;
+  (void)dt;
+  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
+  return plan_select(batch, window, top_k).total;
+}
+
+hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,
+                                float scale, void* out, float* lse, int32_t* sel_idx,
+                                int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                hs2_dtype dt, void* stream) {
+  hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, window, top_k, scale, out, lse, dt);
+  if (st != HS2_OK) return st;
+  if (top_k > 0 && batch->total_q > 0 && !sel_idx)
+    return fail(HS2_ERR_INVALID_ARG, "sel_idx must not be NULL when top_k > 0");
+  if ((sel_idx && !aligned(sel_idx, 4)) || (sel_count && !aligned(sel_count, 4)))
+    return fail(HS2_ERR_INVALID_ARG, "sel_idx and sel_count must be 4-byte aligned");
+  const SelectPlan p = plan_select(batch, window, top_k);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
+                p.total);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (batch->total_q == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = dt == HS2_F32;
+  const int tq = batch->total_q;
+  float* lse2 = at<float>(workspace, p.off_lse2);
+  uint32_t* hist = at<uint32_t>(workspace, p.off_hist);
+  uint32_t* counters = at<uint32_t>(workspace, p.off_counters);
+
+  AttnArgs a{};
+  a.b = to_dev(batch);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sel = nullptr;
+  a.window = window;
+  a.top_k = top_k;
+  a.c2 = scale * kLog2e;
+  a.n_split = p.attn.n_split;
+  a.split_keys = p.attn.split_keys;
+  a.part = p.attn.n_split > 1 ? at<Partial>(workspace, p.off_part) : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.lse2 = lse2;
+  const int grid = tq * p.attn.n_split;
+  hipError_t e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s)
+                     : launch_attn_bf16(a, false, grid, hist, counters, s);
+  if (e != hipSuccess) return hip_fail(e, "full attention launch");
+  if (p.attn.n_split > 1) {
+    CombineArgs c{};
+    c.b = a.b;
+    c.part = a.part;
+    c.n_split = p.attn.n_split;
+    c.split_keys = p.attn.split_keys;
+    c.gather = 0;
+    c.window = window;
+    c.top_k = top_k;
+    c.out = out;
+    c.lse = lse;
+    c.lse2 = lse2;
+    c.hist = hist;
+    c.counters = counters;
+    e = launch_combine(c, f32, s);
+    if (e != hipSuccess) return hip_fail(e, "split combine launch");
+  }
+  TopkArgs tk{};
+  tk.b = a.b;
+  tk.window = window;
+  tk.top_k = top_k;
+  tk.n_split = p.f_split;
+  tk.split_len = p.f_len;
+  tk.score_stride = p.score_stride;
+  tk.scores = top_k > 0 ? at<float>(workspace, p.off_scores) : nullptr;
+  tk.hist = hist;
+  tk.counters = counters;
+  tk.above = top_k > 0 ? at<int32_t>(workspace, p.off_above) : nullptr;
+  tk.cand = top_k > 0 ? at<uint2>(workspace, p.off_cand) : nullptr;
+  tk.sel_idx = sel_idx;
+  tk.sel_count = sel_count;
+  if (top_k > 0) {
+    ScoreArgs sc{};
+    sc.b = a.b;
+    sc.q = q;
+    sc.k = k;
+    sc.lse2 = lse2;
+    sc.c2 = a.c2;
+    sc.window = window;
+    sc.top_k = top_k;
+    sc.n_split = p.score.n_split;
+    sc.split_keys = p.score.split_keys;
+    sc.score_stride = p.score_stride;
+    sc.scores = at<float>(workspace, p.off_scores);
+    sc.hist = hist;
+    e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+  }
+  e = launch_topk(tk, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim, int32_t window,
+                                      int32_t top_k, hs2_dtype dt) {
+  (void)n_heads;
+  (void)head_dim;
+  (void)dt;
+  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
+  return plan_sparse(batch, window, top_k).total;
+}
+
+hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                           const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
+                           int32_t top_k, float scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, window, top_k, scale, out, lse, dt);
+  if (st != HS2_OK) return st;
+  if (top_k > 0 && batch->total_q > 0 && !sel_idx)
+    return fail(HS2_ERR_INVALID_ARG, "sel_idx must not be NULL when top_k > 0");
+  if (sel_idx && !aligned(sel_idx, 4)) return fail(HS2_ERR_INVALID_ARG, "sel_idx must be 4-byte aligned");
+  const SparsePlan p = plan_sparse(batch, window, top_k);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
+                p.total);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (batch->total_q == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = dt == HS2_F32;
+  AttnArgs a{};
+  a.b = to_dev(batch);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sel = sel_idx;
+  a.window = window;
+  a.top_k = top_k;
+  a.c2 = scale * kLog2e;
+  a.n_split = p.attn.n_split;
+  a.split_keys = p.attn.split_keys;
+  a.part = p.attn.n_split > 1 ? static_cast<Partial*>(workspace) : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.lse2 = nullptr;
+  const int grid = batch->total_q * p.attn.n_split;
+  hipError_t e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
+                     : launch_attn_bf16(a, true, grid, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+  if (p.attn.n_split > 1) {
+    CombineArgs c{};
+    c.b = a.b;
+    c.part = a.part;
+    c.n_split = p.attn.n_split;
+    c.split_keys = p.attn.split_keys;
+    c.gather = 1;
+    c.window = window;
+    c.top_k = top_k;
+    c.out = out;
+    c.lse = lse;
+    c.lse2 = nullptr;
+    c.hist = nullptr;
+    c.counters = nullptr;
+    e = launch_combine(c, f32, s);
+    if (e != hipSuccess) return hip_fail(e, "split combine launch");
+  }
+  return ok();
+}
+
+size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t head_dim) {
+  if (d_model <= 0 || n_layers <= 0 || head_dim <= 0) return 0;
+  return align_up((size_t)2 * n_layers * head_dim * d_model * sizeof(uint16_t));
+}
+
+hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                         const void* const* w_k, const void* const* w_v, void* const* k_out,
+                         void* const* v_out, int32_t head_dim, void* workspace, size_t workspace_bytes,
+                         hs2_dtype dt, void* stream) {
+  if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "bridging supports bf16 only");
+  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "bridging supports head_dim=128 only (got %d)", head_dim);
+  if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
+    return fail(HS2_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 65536] (got %d)", d_model);
+  if (n_layers < 1 || n_layers > 8) return fail(HS2_ERR_UNSUPPORTED, "n_layers must be in [1, 8] (got %d)", n_layers);
+  if (n_rows < 0) return fail(HS2_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (!w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARG, "pointer arrays must not be NULL");
+  if (n_rows > 0 && !hidden) return fail(HS2_ERR_INVALID_ARG, "hidden must not be NULL");
+  if (!aligned(hidden, 16)) return fail(HS2_ERR_INVALID_ARG, "hidden must be 16-byte aligned");
+  const uint16_t* w[16];
+  BridgeArgs a{};
+  for (int l = 0; l < n_layers; ++l) {
+    if (!w_k[l] || !w_v[l] || !k_out[l] || !v_out[l])
+      return fail(HS2_ERR_INVALID_ARG, "a weight or output pointer of layer %d is NULL", l);
+    if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_out[l], 16) || !aligned(v_out[l], 16))
+      return fail(HS2_ERR_INVALID_ARG, "weights and outputs must be 16-byte aligned (layer %d)", l);
+    if (k_out[l] == hidden || v_out[l] == hidden) return fail(HS2_ERR_INVALID_ARG, "an output aliases hidden");
+    w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    a.outs[2 * l] = static_cast<uint16_t*>(k_out[l]);
+    a.outs[2 * l + 1] = static_cast<uint16_t*>(v_out[l]);
+  }
+  const size_t need = hs2_bridge_kv_workspace_size(d_model, n_layers, head_dim);
+  if (workspace_bytes < need || !workspace)
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes, need);
+  if (!aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  a.h = static_cast<const uint16_t*>(hidden);
+  a.wt = static_cast<const uint16_t*>(workspace);
+  a.n_rows = n_rows;
+  a.d_model = d_model;
+  a.n_mats = 2 * n_layers;
+  hipError_t e = launch_bridge(a, w, 2 * n_layers, static_cast<uint16_t*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bridging launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Internal declarations shared by the HIP kernels and the host entry points of libhs2.
+// Target: gfx950 (MI355X) only: 64-lane wavefronts, bf16 MFMA 32x32x16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "hs2.h"
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+constexpr int kHeads = 64;     // query heads sharing the single KV head (MQA 64:1)
+constexpr int kDim = 128;      // head_dim
+constexpr int kTile = 32;      // keys per MFMA tile (one 32x32 output block)
+constexpr int kWaves = 4;      // waves per attention workgroup
+constexpr int kHistBits = 12;  // first radix digit: bits 30..19 of a non-negative fp32 score
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 31 - kHistBits;
+constexpr int kCandCap = 8192; // threshold-bin candidates kept per query for the in-LDS select
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device view of the ragged batch descriptor.
+struct SeqsDev {
+  const int64_t* kv_start;
+  const int32_t* kv_len;
+  const int32_t* q_start;
+  const int32_t* q_pos;
+  int32_t num_seqs;
+  int32_t total_q;
+  int64_t total_rows;
+};
+
+// Partial result of one workgroup's key range for one query: running max m (log2
+// domain), softmax denominator l, and the unnormalised output transposed to [dim][head].
+struct Partial {
+  float m[kHeads];
+  float l[kHeads];
+  float o[kDim * kHeads];
+};
+
+// Arguments of the attention kernels (full causal range, or gathered window + selection).
+struct AttnArgs {
+  SeqsDev b;
+  const void* q;          // [total_q][64][128]
+  const void* k;          // [rows][128]
+  const void* v;          // [rows][128]
+  const int32_t* sel;     // gather mode: [total_q][top_k]
+  int32_t window;
+  int32_t top_k;
+  float c2;               // softmax scale * log2(e)
+  int32_t n_split;        // workgroups per query
+  int32_t split_keys;     // logical keys per workgroup (multiple of kTile * kWaves)
+  Partial* part;          // [total_q][n_split] when n_split > 1
+  void* out;              // [total_q][64][128] when n_split == 1
+  float* lse;             // [total_q][64] natural log, nullable (n_split == 1)
+  float* lse2;            // [total_q][64] log2 domain, nullable (n_split == 1)
+};
+
+struct CombineArgs {
+  SeqsDev b;
+  const Partial* part;
+  int32_t n_split;
+  int32_t split_keys;
+  int32_t gather;         // logical key count: t+1 (full) or window+top_k (gather)
+  int32_t window;
+  int32_t top_k;
+  void* out;
+  float* lse;             // nullable
+  float* lse2;            // nullable
+  uint32_t* hist;         // nullable: [total_q][kHistBins] zeroed here for the score pass
+  uint32_t* counters;     // nullable: [total_q][4] zeroed here
+};
+
+struct ScoreArgs {
+  SeqsDev b;
+  const void* q;
+  const void* k;
+  const float* lse2;      // [total_q][64]
+  float c2;
+  int32_t window;
+  int32_t top_k;
+  int32_t n_split;
+  int32_t split_keys;
+  int64_t score_stride;   // floats per query in `scores`
+  float* scores;          // [total_q][score_stride]
+  uint32_t* hist;         // [total_q][kHistBins]
+};
+
+struct TopkArgs {
+  SeqsDev b;
+  int32_t window;
+  int32_t top_k;
+  int32_t n_split;        // filter workgroups per query
+  int32_t split_len;      // candidates per filter workgroup
+  int64_t score_stride;
+  const float* scores;
+  const uint32_t* hist;
+  uint32_t* counters;     // [total_q][4]: 0 = above count, 1 = threshold-bin count
+  int32_t* above;         // [total_q][top_k]
+  uint2* cand;            // [total_q][kCandCap]: (score bits, position)
+  int32_t* sel_idx;       // [total_q][top_k]
+  int32_t* sel_count;     // nullable
+};
+
+struct BridgeArgs {
+  const uint16_t* h;      // [n_rows][d_model]
+  const uint16_t* wt;     // [n_mats][128][d_model]  (transposed weights, workspace)
+  uint16_t* outs[16];     // n_mats output matrices [n_rows][128]
+  int64_t n_rows;
+  int32_t d_model;
+  int32_t n_mats;
+};
+
+// Resolves query i: sequence row base and position t. Returns false when the
+// descriptor is inconsistent (the query is then not computed).
+__device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t) {
+  int lo = 0, hi = b.num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (b.q_start[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  base = b.kv_start[lo];
+  const int n = b.kv_len[lo];
+  t = b.q_pos[i];
+  const bool ok = b.q_start[lo] <= i && i < b.q_start[lo + 1] && t >= 0 && t < n && base >= 0 &&
+                  base + (int64_t)n <= b.total_rows;
+  if (!ok) { base = 0; t = 0; }
+  return ok;
+}
+
+// Number of logical keys of a query: t+1 (full causal) or top_k + min(window, t+1)
+// (gather: selected slots first, then the window rows oldest first).
+__device__ inline int logical_keys(bool gather, int t, int window, int top_k) {
+  return gather ? top_k + min(window, t + 1) : t + 1;
+}
+
+// ---------------------------------------------------------------------------------
+// Host-side launchers (defined next to their kernels).
+// ---------------------------------------------------------------------------------
+hipError_t launch_attn_bf16(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
+                            uint32_t* counters, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
+                           uint32_t* counters, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
+hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_bridge(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats,
+                         uint16_t* wt, hipStream_t s);
+
+}  // namespace hs2

@@ -1,0 +1,232 @@
+"""Thin Python binding of libhs2 (the C ABI in include/hs2.h).
+
+Argument marshalling only: every step of the hot path runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. The functions
+raise if the built library cannot be loaded; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhs2.so")
+
+HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
+HS2_BF16, HS2_F32 = 0, 1
+MAX_TOP_K = 4096
+
+EXPORTED = [
+    "hs2_version",
+    "hs2_last_error",
+    "hs2_bridge_kv_workspace_size",
+    "hs2_bridge_kv",
+    "hs2_full_attn_select_workspace_size",
+    "hs2_full_attn_select",
+    "hs2_sparse_attn_workspace_size",
+    "hs2_sparse_attn",
+]
+
+
+class hs2_seqs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("kv_start", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
+        ("q_start", ctypes.c_void_p),
+        ("q_pos", ctypes.c_void_p),
+        ("total_q", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32),
+        ("total_kv_rows", ctypes.c_int64),
+        ("max_q_per_seq", ctypes.c_int32),
+    ]
+
+
+class HS2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hs2 status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libhs2.so (built in-tree by long_context_mqa_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m long_context_mqa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    SP = ctypes.POINTER(hs2_seqs)
+    lib.hs2_version.restype = I32
+    lib.hs2_version.argtypes = []
+    lib.hs2_last_error.restype = ctypes.c_char_p
+    lib.hs2_last_error.argtypes = []
+    lib.hs2_bridge_kv_workspace_size.restype = SZ
+    lib.hs2_bridge_kv_workspace_size.argtypes = [I32, I32, I32]
+    lib.hs2_bridge_kv.restype = I32
+    lib.hs2_bridge_kv.argtypes = [P, I64, I32, I32, P, P, P, P, I32, P, SZ, I32, P]
+    lib.hs2_full_attn_select_workspace_size.restype = SZ
+    lib.hs2_full_attn_select_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
+    lib.hs2_full_attn_select.restype = I32
+    lib.hs2_full_attn_select.argtypes = [SP, P, P, P, I32, I32, I32, I32, F, P, P, P, P, P, SZ, I32, P]
+    lib.hs2_sparse_attn_workspace_size.restype = SZ
+    lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
+    lib.hs2_sparse_attn.restype = I32
+    lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    _lib = lib
+    return lib
+
+
+def _check(st: int) -> None:
+    if st != HS2_OK:
+        raise HS2Error(st, load().hs2_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HS2_BF16
+    if t.dtype == torch.float32:
+        return HS2_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Batch:
+    """A ragged batch: device descriptor arrays plus the host sizes the library needs."""
+
+    kv_start: torch.Tensor   # int64 [S]
+    kv_len: torch.Tensor     # int32 [S]
+    q_start: torch.Tensor    # int32 [S+1]
+    q_pos: torch.Tensor      # int32 [total_q]
+    total_q: int
+    max_kv_len: int
+    total_kv_rows: int
+    max_q_per_seq: int
+
+    def c(self) -> hs2_seqs:
+        return hs2_seqs(int(self.kv_start.numel()), _ptr(self.kv_start), _ptr(self.kv_len), _ptr(self.q_start),
+                        _ptr(self.q_pos), int(self.total_q), int(self.max_kv_len), int(self.total_kv_rows),
+                        int(self.max_q_per_seq))
+
+    @staticmethod
+    def from_host(kv_start, kv_len, q_start, q_pos, total_kv_rows: int, device="cuda") -> "Batch":
+        """Builds the device descriptor from host sequences (numpy or lists)."""
+        ks = torch.as_tensor(kv_start, dtype=torch.int64)
+        kl = torch.as_tensor(kv_len, dtype=torch.int32)
+        qs = torch.as_tensor(q_start, dtype=torch.int32)
+        qp = torch.as_tensor(q_pos, dtype=torch.int32)
+        per = (qs[1:] - qs[:-1]) if qs.numel() > 1 else torch.zeros(1, dtype=torch.int32)
+        return Batch(ks.to(device), kl.to(device), qs.to(device), qp.to(device), int(qp.numel()),
+                     max(1, int(kl.max().item()) if kl.numel() else 1), int(total_kv_rows),
+                     int(per.max().item()) if per.numel() else 0)
+
+
+def full_attn_select_workspace_size(batch: Batch, window: int, top_k: int, dtype=torch.bfloat16) -> int:
+    b = batch.c()
+    return int(load().hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, window, top_k,
+                                                          HS2_BF16 if dtype == torch.bfloat16 else HS2_F32))
+
+
+def sparse_attn_workspace_size(batch: Batch, window: int, top_k: int, dtype=torch.bfloat16) -> int:
+    b = batch.c()
+    return int(load().hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k,
+                                                     HS2_BF16 if dtype == torch.bfloat16 else HS2_F32))
+
+
+def bridge_kv_workspace_size(d_model: int, n_layers: int, head_dim: int = 128) -> int:
+    return int(load().hs2_bridge_kv_workspace_size(d_model, n_layers, head_dim))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def full_attn_select(batch: Batch, q, k, v, window: int = 128, top_k: int = 1024, scale: float | None = None,
+                     out=None, lse=None, sel_idx=None, sel_count=None, workspace=None, stream=None,
+                     want_lse: bool = True):
+    """hs2_full_attn_select: exact causal MQA attention plus top-k selection per query.
+
+    Returns (out [total_q, 64, 128], lse [total_q, 64] or None, sel_idx [total_q, top_k], sel_count [total_q]).
+    """
+    lib = load()
+    dt = _dtype_code(q)
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(batch.total_q, 64, dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty(batch.total_q, max(top_k, 0), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty(batch.total_q, dtype=torch.int32, device=dev)
+    b = batch.c()
+    need = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, window, top_k, dt)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check(lib.hs2_full_attn_select(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), q.shape[1], q.shape[2], window,
+                                    top_k, scale, _ptr(out), _ptr(lse), _ptr(sel_idx) if top_k > 0 else None,
+                                    _ptr(sel_count), _ptr(workspace), workspace.numel(), dt, _stream(stream)))
+    return out, lse, sel_idx, sel_count
+
+
+def sparse_attn(batch: Batch, q, k, v, sel_idx, window: int = 128, top_k: int | None = None,
+                scale: float | None = None, out=None, lse=None, workspace=None, stream=None):
+    """hs2_sparse_attn: attention over the window plus the selected rows. Returns (out, lse)."""
+    lib = load()
+    dt = _dtype_code(q)
+    if top_k is None:
+        top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    b = batch.c()
+    need = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib.hs2_sparse_attn(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx) if top_k > 0 else None,
+                               q.shape[1], q.shape[2], window, top_k, scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                               workspace.numel(), dt, _stream(stream)))
+    return out, lse
+
+
+def bridge_kv(hidden, w_k: list, w_v: list, k_out: list | None = None, v_out: list | None = None,
+              workspace=None, stream=None):
+    """hs2_bridge_kv: K_l = H W_K^l, V_l = H W_V^l for every layer, one pass over H."""
+    lib = load()
+    n_rows, d_model = hidden.shape
+    L = len(w_k)
+    head_dim = w_k[0].shape[1]
+    if k_out is None:
+        k_out = [torch.empty(n_rows, head_dim, dtype=hidden.dtype, device=hidden.device) for _ in range(L)]
+    if v_out is None:
+        v_out = [torch.empty(n_rows, head_dim, dtype=hidden.dtype, device=hidden.device) for _ in range(L)]
+    arr = ctypes.c_void_p * L
+    wk = arr(*[w.data_ptr() for w in w_k])
+    wv = arr(*[w.data_ptr() for w in w_v])
+    ko = arr(*[t.data_ptr() for t in k_out])
+    vo = arr(*[t.data_ptr() for t in v_out])
+    need = lib.hs2_bridge_kv_workspace_size(d_model, L, head_dim)
+    if workspace is None:
+        workspace = _workspace(need, hidden.device)
+    _check(lib.hs2_bridge_kv(_ptr(hidden), n_rows, d_model, L, wk, wv, ko, vo, head_dim, _ptr(workspace),
+                             workspace.numel(), _dtype_code(hidden), _stream(stream)))
+    return k_out, v_out

@@ -1,0 +1,94 @@
+"""Parity helpers shared by the GPU tests: device upload and the comparison rules.
+
+Comparison rules:
+  * index sets: every oracle-selected key whose score exceeds tau*(1+1e-5) must be in
+    the GPU set, no key scoring below tau*(1-1e-5) may be in it (tau = the oracle's
+    k-th score), the sizes must be equal (min(k, candidates)), and the GPU set must be
+    ascending without duplicates. Without a tau (all candidates taken) the sets must
+    be equal.
+  * attention outputs (full and sparse): max |gpu - fp64| <= 1e-2 and mean <= 1e-3,
+    the GPU value taken in its output dtype.
+  * LSE: |gpu - fp64| <= 1e-3 (fp32 output of a value of magnitude ~10).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from workloads.gen import stored_to_f64
+
+REL_BAND = 1e-5
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+LSE_ABS = 1e-3
+
+
+def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_selection(gpu_sel: np.ndarray, gpu_count: int, ref: dict, top_k: int, nc: int, what: str = ""):
+    k_eff = min(top_k, nc)
+    assert gpu_count == k_eff, f"{what}: count {gpu_count} != {k_eff}"
+    sel = np.asarray(gpu_sel[:k_eff], dtype=np.int64)
+    assert np.all(np.asarray(gpu_sel[k_eff:]) == -1), f"{what}: padding is not -1"
+    if k_eff:
+        assert np.all(np.diff(sel) > 0), f"{what}: not strictly ascending"
+        assert sel[0] >= 0 and sel[-1] < nc, f"{what}: index outside the candidates"
+    tau = ref["tau"]
+    if tau is None:
+        assert sel.tolist() == ref["sel"].tolist(), f"{what}: selection differs (all candidates expected)"
+        return 0
+    scores = ref["scores"]
+    must = ref["sel"][scores[ref["sel"]] > tau * (1 + REL_BAND)]
+    missing = np.setdiff1d(must, sel)
+    assert missing.size == 0, f"{what}: {missing.size} clearly-selected keys missing, e.g. {missing[:5]}"
+    bad = sel[scores[sel] < tau * (1 - REL_BAND)]
+    assert bad.size == 0, f"{what}: {bad.size} clearly-unselected keys chosen, e.g. {bad[:5]}"
+    return int(np.setdiff1d(sel, ref["sel"]).size)  # keys swapped inside the tolerance band
+
+
+def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
+    err = np.abs(gpu - ref)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    assert err.max() <= MAX_ABS, f"{what}: max abs err {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean abs err {err.mean():.3e}"
+    return float(err.max()), float(err.mean())
+
+
+def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
+    err = np.abs(gpu - ref)
+    assert err.max() <= LSE_ABS, f"{what}: lse max abs err {err.max():.3e}"
+
+
+def oracle_query(inp, qi: int):
+    """fp64 oracle of query qi's selector, from the stored inputs."""
+    s = int(inp.q_seq[qi])
+    a = int(inp.kv_start[s])
+    t = int(inp.q_pos[qi])
+    K = stored_to_f64(inp.k[a:a + t + 1])
+    V = stored_to_f64(inp.v[a:a + t + 1])
+    Q = stored_to_f64(inp.q_sel[qi])
+    sp = inp.spec
+    r = oracle.selector_query(Q, K, V, t, sp.window, sp.top_k, sp.scale)
+    r["K"], r["V"], r["t"] = K, V, t
+    return r
+
+
+def oracle_sparse(inp, qi: int, layer: int, sel: np.ndarray, K=None, V=None):
+    s = int(inp.q_seq[qi])
+    a = int(inp.kv_start[s])
+    t = int(inp.q_pos[qi])
+    if K is None:
+        K = stored_to_f64(inp.k[a:a + t + 1])
+        V = stored_to_f64(inp.v[a:a + t + 1])
+    Q = stored_to_f64(inp.q_sp[layer][qi])
+    sp = inp.spec
+    return oracle.sparse_attention(Q, K, V, t, sel, sp.window, sp.scale)

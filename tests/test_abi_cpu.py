@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/hs2.h
+declares, and rejects bad arguments on the host before enqueueing anything.
+
+Every call here fails a host-side check, so no HIP call is made; the pointers
+passed are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_mqa_amd import hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs2.h")
+FAKE = 0x10000  # a non-null, 256-byte aligned address that is never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs2.LIB_PATH):
+        from long_context_mqa_amd import build
+        build.build()
+    return hs2.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(hs2.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert lib.hs2_version() == 10000
+
+
+def _batch(total_q=1, max_kv_len=4096, rows=4096, num_seqs=1):
+    return hs2.hs2_seqs(num_seqs, FAKE, FAKE, FAKE, FAKE, total_q, max_kv_len, rows, 1)
+
+
+def _select(lib, b, n_heads=64, head_dim=128, window=128, top_k=1024, scale=0.088, ws=None, ws_bytes=None,
+            dt=hs2.HS2_BF16, q=FAKE, out=FAKE * 2, sel=FAKE * 3):
+    if ws_bytes is None:
+        ws_bytes = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b), n_heads, head_dim, window, top_k, dt)
+    return lib.hs2_full_attn_select(ctypes.byref(b), q, FAKE, FAKE, n_heads, head_dim, window, top_k, scale, out,
+                                    None, sel, None, FAKE if ws is None else ws, ws_bytes, dt, None)
+
+
+def test_select_rejects_bad_arguments(lib):
+    b = _batch()
+    assert _select(lib, b, n_heads=32) == hs2.HS2_ERR_UNSUPPORTED
+    assert b"n_heads=64" in lib.hs2_last_error()
+    assert _select(lib, b, head_dim=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert _select(lib, b, dt=7) == hs2.HS2_ERR_UNSUPPORTED
+    assert _select(lib, b, window=0) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, top_k=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, top_k=hs2.MAX_TOP_K + 1) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, scale=0.0) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, scale=float("nan")) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, q=FAKE + 8) == hs2.HS2_ERR_INVALID_ARG        # misaligned
+    assert _select(lib, b, out=FAKE) == hs2.HS2_ERR_INVALID_ARG          # aliases k
+    assert _select(lib, b, sel=None) == hs2.HS2_ERR_INVALID_ARG
+    assert _select(lib, b, ws_bytes=16) == hs2.HS2_ERR_WORKSPACE
+    assert b"workspace" in lib.hs2_last_error()
+    assert _select(lib, b, ws=FAKE + 64, ws_bytes=1 << 40) == hs2.HS2_ERR_WORKSPACE  # misaligned
+    assert lib.hs2_full_attn_select(None, FAKE, FAKE, FAKE, 64, 128, 128, 1024, 0.1, FAKE, None, FAKE, None,
+                                    FAKE, 1 << 30, 0, None) == hs2.HS2_ERR_INVALID_ARG
+    bad = hs2.hs2_seqs(0, FAKE, FAKE, FAKE, FAKE, 1, 10, 10, 1)
+    assert _select(lib, bad) == hs2.HS2_ERR_INVALID_ARG
+    bad = hs2.hs2_seqs(1, None, FAKE, FAKE, FAKE, 1, 10, 10, 1)
+    assert _select(lib, bad) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_sparse_rejects_bad_arguments(lib):
+    b = _batch()
+    ws = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, 128, 1024, 0)
+    assert ws > 0  # one query is split over several workgroups
+    call = lambda **kw: lib.hs2_sparse_attn(ctypes.byref(b), FAKE, FAKE, FAKE, kw.get("sel", FAKE * 3), 64,
+                                            kw.get("hd", 128), 128, kw.get("k", 1024), 0.088, FAKE * 2, None,
+                                            FAKE, kw.get("ws", ws), 0, None)
+    assert call(hd=96) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(sel=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws=ws - 1) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_bridge_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p * 3
+    w = P(FAKE, FAKE, FAKE)
+    o = P(FAKE * 2, FAKE * 3, FAKE * 4)
+    ws = lib.hs2_bridge_kv_workspace_size(2048, 3, 128)
+    assert ws == 2 * 3 * 128 * 2048 * 2
+    ok_args = dict(h=FAKE * 5, n=1000, d=2048, L=3, hd=128, ws=ws, dt=0)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return lib.hs2_bridge_kv(a["h"], a["n"], a["d"], a["L"], w, w, o, o, a["hd"], FAKE * 8, a["ws"], a["dt"],
+                                 None)
+    assert call(dt=1) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(hd=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(d=2000) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(L=9) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(n=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(h=FAKE * 5 + 2) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws=ws - 2) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_workspace_sizes_grow_with_the_batch(lib):
+    small = _batch(total_q=4, max_kv_len=8192, rows=8192 * 4, num_seqs=4)
+    big = _batch(total_q=64, max_kv_len=131072, rows=131072 * 64, num_seqs=64)
+    s = lib.hs2_full_attn_select_workspace_size(ctypes.byref(small), 64, 128, 128, 1024, 0)
+    g = lib.hs2_full_attn_select_workspace_size(ctypes.byref(big), 64, 128, 128, 1024, 0)
+    assert 0 < s < g
+    # scores of every candidate of every query fit
+    assert g >= 64 * (131072 - 127) * 4
+    assert lib.hs2_full_attn_select_workspace_size(None, 64, 128, 128, 1024, 0) == 0

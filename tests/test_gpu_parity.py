@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases are checked on every output element; the five workloads at full size
+are checked on sampled queries (every output of a sampled query) plus properties
+that hold for every query (counts, ordering, planted needles).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_mqa_amd import hs2
+from tests.parity import (check_attn, check_lse, check_selection, from_dev, oracle_query, oracle_sparse,
+                          to_dev)
+from workloads.configs import BlockSpec, block_config, make_block_inputs, make_bridge_inputs
+from workloads.gen import bf16_round, bf16_to_f32, stored_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_block(inp, selector_only=False):
+    """Runs the selector and every sparse layer of a block on the GPU."""
+    sp = inp.spec
+    dev = "cuda"
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, sp.total_rows, dev)
+    k = to_dev(inp.k)
+    v = to_dev(inp.v)
+    q = to_dev(inp.q_sel)
+    out, lse, sel, cnt = hs2.full_attn_select(batch, q, k, v, sp.window, sp.top_k, sp.scale)
+    sparse = []
+    if not selector_only:
+        for l in range(sp.n_sparse):
+            qs = to_dev(inp.q_sp[l])
+            o, _ = hs2.sparse_attn(batch, qs, k, v, sel, sp.window, sp.top_k, sp.scale)
+            sparse.append(from_dev(o))
+    torch.cuda.synchronize()
+    return {"out": from_dev(out), "lse": from_dev(lse), "sel": sel.cpu().numpy(), "count": cnt.cpu().numpy(),
+            "sparse": sparse, "batch": batch, "k": k, "v": v}
+
+
+def check_queries(inp, g, qis, what):
+    sp = inp.spec
+    swapped = 0
+    for qi in qis:
+        r = oracle_query(inp, qi)
+        t = r["t"]
+        nc = oracle.candidate_count(t, sp.window)
+        tag = f"{what} q{qi} t={t}"
+        check_attn(g["out"][qi], r["out"], tag + " selector out")
+        check_lse(g["lse"][qi], r["lse"], tag)
+        swapped += check_selection(g["sel"][qi], int(g["count"][qi]), r, sp.top_k, nc, tag)
+        for l, o in enumerate(g["sparse"]):
+            ref, _ = oracle_sparse(inp, qi, l, g["sel"][qi], r["K"], r["V"])
+            check_attn(o[qi], ref, tag + f" sparse layer {l}")
+    return swapped
+
+
+def check_all_queries_properties(inp, g):
+    sp = inp.spec
+    for qi in range(sp.total_q):
+        t = int(inp.q_pos[qi])
+        nc = max(0, t - sp.window + 1)
+        k_eff = min(sp.top_k, nc)
+        assert int(g["count"][qi]) == k_eff
+        s = g["sel"][qi][:k_eff]
+        assert np.all(np.diff(s) > 0) and (k_eff == 0 or (s[0] >= 0 and s[-1] < nc))
+        assert np.all(g["sel"][qi][k_eff:] == -1)
+    for (si, qi, h, p) in inp.needles:
+        assert p in set(g["sel"][qi].tolist()), f"needle at {p} of query {qi} not selected"
+    assert np.isfinite(g["out"]).all()
+    for o in g["sparse"]:
+        assert np.isfinite(o).all()
+
+
+# ----------------------------------------------------------------------------------
+# small cases: every output checked
+# ----------------------------------------------------------------------------------
+
+def test_tiny_block_f32():
+    """Workload 1: 1 seq x 4096, 16 queries, fp32, selector + 2 sparse layers."""
+    inp = make_block_inputs(block_config(1))
+    _say("tiny f32 block")
+    g = run_block(inp)
+    check_queries(inp, g, range(inp.spec.total_q), "tiny-f32")
+    check_all_queries_properties(inp, g)
+
+
+def test_tiny_block_bf16():
+    inp = make_block_inputs(block_config(1, dtype="bf16", seed=11))
+    _say("tiny bf16 block")
+    g = run_block(inp)
+    check_queries(inp, g, range(inp.spec.total_q), "tiny-bf16")
+    check_all_queries_properties(inp, g)
+
+
+RAGGED = BlockSpec(
+    "ragged-small", [700, 1152, 1153, 3000, 9000, 40000],
+    [[699, 100, 0], [1151], [1152], [2999, 2000], [8999, 5000, 127, 128, 1151, 1152], [39999]],
+    dtype="bf16", n_sparse=2, needles_per_query=2, seed=12)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_small_contexts(dtype):
+    """Several sequences and queries per sequence; t < window, candidates <= k and > k."""
+    spec = BlockSpec(**{**RAGGED.__dict__, "dtype": dtype})
+    inp = make_block_inputs(spec)
+    _say(f"ragged small {dtype}")
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), f"ragged-{dtype}")
+    check_all_queries_properties(inp, g)
+
+
+def test_small_context_sparse_equals_full_on_gpu():
+    """When t+1 <= window + top_k, the sparse layer with the selector's own Q reproduces
+    the selector's output (the <= 1,152-row invariant)."""
+    spec = BlockSpec("inv", [1152, 900, 5000], [[1151, 1000, 64], [899], [1151]], dtype="bf16", n_sparse=0,
+                     needles_per_query=0, seed=13)
+    inp = make_block_inputs(spec)
+    g = run_block(inp, selector_only=True)
+    q = to_dev(inp.q_sel)
+    o, _ = hs2.sparse_attn(g["batch"], q, g["k"], g["v"], torch.from_numpy(g["sel"]).cuda(), spec.window, spec.top_k,
+                           spec.scale)
+    o = from_dev(o)
+    for qi in range(spec.total_q):
+        check_attn(o[qi], g["out"][qi], f"invariant q{qi}")
+        r = oracle_query(inp, qi)
+        check_attn(o[qi], r["out"], f"invariant-vs-oracle q{qi}")
+
+
+def test_top_k_zero_and_window_one():
+    spec = BlockSpec("k0", [3000, 500], [[2999, 10], [499]], dtype="bf16", n_sparse=1, needles_per_query=0,
+                     seed=14, top_k=0, window=1)
+    inp = make_block_inputs(spec)
+    g = run_block(inp)
+    assert np.all(g["count"] == 0)
+    for qi in range(spec.total_q):
+        r = oracle_query(inp, qi)
+        check_attn(g["out"][qi], r["out"], f"k0 q{qi}")
+        ref, _ = oracle_sparse(inp, qi, 0, np.zeros(0, dtype=np.int64), r["K"], r["V"])
+        check_attn(g["sparse"][0][qi], ref, f"k0 sparse q{qi}")
+
+
+def test_window_and_k_small():
+    spec = BlockSpec("w5k7", [2000, 40], [[1999, 600], [39]], dtype="bf16", n_sparse=1, needles_per_query=1,
+                     seed=15, top_k=7, window=5)
+    inp = make_block_inputs(spec)
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), "w5k7")
+    check_all_queries_properties(inp, g)
+
+
+def test_exact_ties_prefer_smaller_position():
+    """Identical key rows give bitwise-equal scores; the k-th place must go to the
+    smallest positions among them."""
+    spec = BlockSpec("ties", [6000], [[5999]], dtype="bf16", n_sparse=1, needles_per_query=0, seed=16,
+                     top_k=16)
+    inp = make_block_inputs(spec)
+    # 40 identical strong rows at spread positions: only the 16 smallest may be chosen
+    qv = bf16_to_f32(inp.q_sel[0]).astype(np.float64).mean(axis=0)
+    strong = (8.0 * qv / np.linalg.norm(qv) * math.sqrt(128)).astype(np.float32)
+    row = bf16_round(strong)
+    pos = np.arange(100, 100 + 40 * 97, 97)
+    inp.k[pos] = row
+    g = run_block(inp)
+    r = oracle_query(inp, 0)
+    assert r["sel"].tolist() == pos[:16].tolist()
+    assert g["sel"][0].tolist() == pos[:16].tolist()
+    ref, _ = oracle_sparse(inp, 0, 0, g["sel"][0], r["K"], r["V"])
+    check_attn(g["sparse"][0][0], ref, "ties sparse")
+
+
+def test_invalid_descriptor_is_not_computed():
+    """A query whose position lies outside its sequence is skipped: NaN outputs and
+    sel_count -1; the other queries are unaffected."""
+    spec = BlockSpec("bad", [3000, 2000], [[2999], [1999]], dtype="bf16", n_sparse=1, needles_per_query=0,
+                     seed=17)
+    inp = make_block_inputs(spec)
+    inp.q_pos[1] = 2500  # beyond kv_len of sequence 1
+    g = run_block(inp)
+    assert int(g["count"][1]) == -1
+    assert np.isnan(g["out"][1]).all()
+    assert np.all(g["sel"][1] == -1)
+    assert np.isnan(g["sparse"][0][1]).all()
+    r = oracle_query(inp, 0)
+    check_attn(g["out"][0], r["out"], "valid neighbour")
+    check_selection(g["sel"][0], int(g["count"][0]), r, spec.top_k, 3000 - 127, "valid neighbour")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    inp = make_block_inputs(BlockSpec("det", [20000, 7000], [[19999], [6999, 3000]], dtype="bf16", n_sparse=1,
+                                      needles_per_query=4, seed=18))
+    a = run_block(inp)
+    b = run_block(inp)
+    assert np.array_equal(a["sel"], b["sel"])
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["sparse"][0], b["sparse"][0])
+
+
+BRIDGE_ATOL = 2.0 ** -14
+
+
+def _bridge_check(bi, gk, gv, rows):
+    H = stored_to_f64(bi.h[rows])
+    ks, vs = oracle.bridge_kv(H, [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v])
+    for l in range(len(bi.w_k)):
+        for got, ref in ((gk[l], ks[l]), (gv[l], vs[l])):
+            g = from_dev(got[torch.as_tensor(rows, device=got.device)])
+            # 1 bf16 ulp of the reference value, plus the absolute error of an fp32
+            # accumulation of d_model products (matters only for outputs near zero)
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            err = np.abs(g - ref)
+            bad = err > ulp + BRIDGE_ATOL
+            assert not bad.any(), (f"bridge layer {l}: {bad.sum()} values beyond tolerance, worst err "
+                                   f"{err[bad].max():.3e} at |ref| {np.abs(ref[bad]).min():.3e}")
+            # against the correctly rounded bf16 value: bf16 output quantisation alone gives a
+            # mean |error| of ~1e-3 against fp64 for outputs of this size, so the closeness
+            # test is made against RNE_bf16(reference)
+            ref_b = bf16_to_f32(bf16_round(ref.astype(np.float32))).astype(np.float64)
+            mism = g != ref_b
+            assert mism.mean() <= 1e-2, f"bridge layer {l}: {mism.mean():.2%} differ from the rounded reference"
+            assert np.abs(g - ref_b).mean() <= 1e-4
+
+
+def test_bridge_small_ragged_rows():
+    bi = make_bridge_inputs(1000, n_layers=3, seed=21)
+    h = to_dev(bi.h)
+    gk, gv = hs2.bridge_kv(h, [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v])
+    torch.cuda.synchronize()
+    _bridge_check(bi, gk, gv, np.arange(1000))
+
+
+def test_bridge_one_layer_and_tiny_rows():
+    bi = make_bridge_inputs(37, n_layers=1, seed=22, d_model=256)
+    gk, gv = hs2.bridge_kv(to_dev(bi.h), [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v])
+    torch.cuda.synchronize()
+    _bridge_check(bi, gk, gv, np.arange(37))
+
+
+# ----------------------------------------------------------------------------------
+# the workloads at full size: sampled queries + properties of every query
+# ----------------------------------------------------------------------------------
+
+def _full(n, sample):
+    spec = block_config(n)
+    _say(f"workload {n}: generating {spec.name}")
+    inp = make_block_inputs(spec)
+    _say(f"workload {n}: running")
+    g = run_block(inp)
+    _say(f"workload {n}: checking")
+    check_all_queries_properties(inp, g)
+    check_queries(inp, g, sample, spec.name)
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_workload2_decode_64x128k():
+    _full(2, [0, 37, 63])
+
+
+def test_workload3_decode_8x1m():
+    _full(3, [0, 7])
+
+
+def test_workload4_chunk_4096_queries():
+    _full(4, [0, 2048, 4095])
+
+
+def test_workload5_bridge_and_ragged_decode():
+    bi = make_bridge_inputs(1048576, n_layers=3, seed=5)
+    _say("workload 5: bridging 1M x 2048 -> 3 layers")
+    h = to_dev(bi.h)
+    gk, gv = hs2.bridge_kv(h, [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v])
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 300), np.random.default_rng(0).choice(1048576, 300, replace=False),
+                           np.arange(1048576 - 300, 1048576)])
+    _bridge_check(bi, gk, gv, rows)
+    del h, gk, gv
+    torch.cuda.empty_cache()
+    _full(5, [0, 13, 31])
