@@ -1,0 +1,287 @@
+#!/usr/bin/env python
+"""Benchmark of the HySparse2 attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input resident in HBM:
+the full-attention selector (exact causal MQA attention, head-summed scores, top-1024
+selection) followed by every sparse layer of the hybrid block on the selector's KV and
+indices. The default workload is batched decode: 64 sequences x 131,072 cached tokens,
+one query each, 1 selector + 7 sparse layers (bf16). `--workload 3/4/5` measures the
+other workloads (5 also runs the KV Bridging projection of 1,048,576 hidden states).
+
+Prints ONE JSON line. Per-kernel durations come from HIP events recorded by the
+library around each kernel it launches, on the stream it launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode tokens/s & HBM GB/s at 128k/1M ctx; select+attn TFLOP/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+KV_ROW_BYTES = 2 * 128 * 2          # one K row + one V row, bf16
+QO_BYTES = 2 * 64 * 128 * 2         # one query's Q and O, bf16
+QK_PV_FLOPS = 2 * 2 * 64 * 128      # per (query, key): QK^T and PV over 64 heads
+SCORE_FLOPS = 2 * 64 * 128          # per candidate: the score pass recomputes QK^T
+COUNTERS = os.path.join(ROOT, "profiles", "attn_pass1_decode_64x128k_counters.json")
+SELECT_KERNELS = ["attn_pass1", "split_combine", "score_pass2", "topk_filter", "topk_finish"]
+SPARSE_KERNELS = ["sparse_attn", "sparse_combine"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "hs2_internal.h"):
+        with open(os.path.join(ROOT, "long_context_mqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(per_launch_keys: int):
+    """HBM bytes of one pass-1 launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except OSError:
+        return None
+    if c.get("source_digest") != source_digest() or c.get("keys_per_launch") != per_launch_keys:
+        return None
+    return float(c["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle, unchanged, on a bounded sample of the same workload's queries."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads.gen import stored_to_f64
+
+    sp = inp.spec
+    order = list(range(sp.total_q))
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done, spent = 0, 0.0
+    for qi in order:
+        s = int(inp.q_seq[qi])
+        a, t = int(inp.kv_start[s]), int(inp.q_pos[qi])
+        K = stored_to_f64(inp.k[a:a + t + 1])
+        V = stored_to_f64(inp.v[a:a + t + 1])
+        q = stored_to_f64(inp.q_sel[qi])
+        qs = [stored_to_f64(x[qi]) for x in inp.q_sp]
+        t0 = time.perf_counter()
+        oracle.block_query(q, qs, K, V, t, sp.window, sp.top_k, sp.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {sp.total_q} queries of {sp.name} (selector + {sp.n_sparse} sparse layers "
+                      f"each, fp64, {spent:.1f} s)"}
+
+
+def to_dev(a, device="cuda"):
+    """Uploads stored values (bf16 bit patterns as uint16, or float32) to the GPU."""
+    import numpy as np
+    import torch
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a "
+              f"single MI355X; multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from long_context_mqa_amd import hs2
+    from workloads.configs import block_config, make_bridge_inputs, make_block_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hs2.load()
+    spec = block_config(args.workload)
+    log(f"generating {spec.name}")
+    inp = make_block_inputs(spec)
+    dev = torch.device("cuda:0")
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, dev)
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    q_sel = to_dev(inp.q_sel)
+    q_sp = [to_dev(x) for x in inp.q_sp]
+    nq = spec.total_q
+    out = torch.empty_like(q_sel)
+    lse = torch.empty(nq, 64, dtype=torch.float32, device=dev)
+    sel = torch.empty(nq, spec.top_k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k), dtype=torch.uint8,
+                         device=dev)
+    ws_sp = torch.empty(max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k)), dtype=torch.uint8,
+                        device=dev)
+    outs = [torch.empty_like(q_sel) for _ in range(spec.n_sparse)]
+    bridge = None
+    if args.workload == 5:
+        log("generating bridging inputs (1,048,576 x 2048)")
+        bi = make_bridge_inputs(1048576, n_layers=3, seed=5)
+        bridge = {"h": to_dev(bi.h), "wk": [to_dev(w) for w in bi.w_k], "wv": [to_dev(w) for w in bi.w_v]}
+        bridge["ko"] = [torch.empty(1048576, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        bridge["vo"] = [torch.empty(1048576, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        bridge["ws"] = torch.empty(hs2.bridge_kv_workspace_size(2048, 3), dtype=torch.uint8, device=dev)
+        del bi
+    torch.cuda.synchronize()
+
+    def new_events(n):
+        """2n timing events plus a start marker; all recorded once so the HIP events exist."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
+        s = torch.cuda.current_stream()
+        for e in evs:
+            e.record(s)
+        return evs
+
+    def attach(evs):
+        if evs is None:
+            hs2.set_kernel_events(None)
+            return
+        evs[-1].record(torch.cuda.current_stream())   # start marker of this call
+        hs2.set_kernel_events([e.cuda_event for e in evs[:-1]])
+
+    def step(ev_sel=None, ev_sp=None, ev_br=None):
+        if bridge is not None:
+            attach(ev_br)
+            hs2.bridge_kv(bridge["h"], bridge["wk"], bridge["wv"], bridge["ko"], bridge["vo"], workspace=bridge["ws"])
+        attach(ev_sel)
+        hs2.full_attn_select(batch, q_sel, k, v, spec.window, spec.top_k, spec.scale, out=out, lse=lse,
+                             sel_idx=sel, sel_count=cnt, workspace=ws_sel)
+        for l in range(spec.n_sparse):
+            attach(ev_sp[l] if ev_sp else None)
+            hs2.sparse_attn(batch, q_sp[l], k, v, sel, spec.window, spec.top_k, spec.scale, out=outs[l],
+                            workspace=ws_sp)
+        hs2.set_kernel_events(None)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(new_events(5), [new_events(2) for _ in range(spec.n_sparse)], new_events(2) if bridge else None)
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(*ev[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+
+    def mean_ms(calls, j):
+        """Mean duration of slot j over the calls that launched it (None if none did)."""
+        vals = [c[2 * j].elapsed_time(c[2 * j + 1]) for c in calls if c[-1].elapsed_time(c[2 * j]) >= 0.0]
+        return float(np.mean(vals)) if vals else None
+
+    sel_calls = [e[0] for e in ev]
+    kern = {name: mean_ms(sel_calls, j) for j, name in enumerate(SELECT_KERNELS)}
+    if spec.n_sparse:
+        sp_calls = [ev[s_][1][l] for s_ in range(args.steps) for l in range(spec.n_sparse)]
+        kern["sparse_attn"] = mean_ms(sp_calls, 0)
+        kern["sparse_combine"] = mean_ms(sp_calls, 1)
+    if bridge is not None:
+        br = [e[2] for e in ev]
+        kern["bridge_transpose"] = mean_ms(br, 0)
+        kern["bridge_gemm"] = mean_ms(br, 1)
+    sparse_layer_ms = (kern.get("sparse_attn") or 0.0) + (kern.get("sparse_combine") or 0.0)
+
+    # algorithmic work
+    keys = int(sum(int(t) + 1 for t in inp.q_pos))
+    cands = int(sum(max(0, int(t) - spec.window + 1) for t in inp.q_pos))
+    attended = int(sum(min(int(t) + 1, spec.window + spec.top_k) for t in inp.q_pos))
+    sel_bytes = keys * KV_ROW_BYTES if nq == spec.total_q and all(len(p) == 1 for p in spec.q_positions) \
+        else spec.total_rows * KV_ROW_BYTES
+    sparse_bytes = spec.n_sparse * (attended * KV_ROW_BYTES + nq * QO_BYTES)
+    step_bytes = sel_bytes + sparse_bytes
+    flops_attn = keys * QK_PV_FLOPS + spec.n_sparse * attended * QK_PV_FLOPS
+    flops_score = cands * SCORE_FLOPS
+    decode = all(len(p) == 1 for p in spec.q_positions)
+    res = {
+        "metric": METRIC,
+        "value": nq / (elapsed / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V (bf16) with planted needle keys",
+        "config": {"workload": spec.name, "seqs": len(spec.seq_lens), "queries": nq,
+                   "ctx": int(max(spec.seq_lens)), "sparse_layers": spec.n_sparse, "window": spec.window,
+                   "top_k": spec.top_k, "q_heads": 64, "kv_heads": 1, "head_dim": 128,
+                   "parallelism": "single GPU"},
+    }
+    if args.workload == 5:
+        res["config"]["bridging"] = {"rows": 1048576, "d_model": 2048, "layers": 3}
+    if decode:
+        a_bytes = keys * KV_ROW_BYTES
+        res["roofline"] = {"kernel": "attn_pass1 (selector exact attention, K+V once)", "bound": "hbm",
+                           "achieved": a_bytes / (kern["attn_pass1"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": a_bytes / (kern["attn_pass1"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                           "traffic": counter_traffic(keys) if args.workload == 2 else None,
+                           "alg_bytes_per_launch": a_bytes}
+    else:
+        f = keys * QK_PV_FLOPS
+        ach = f / (kern["attn_pass1"] * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "attn_pass1 (selector exact attention)", "bound": "mfma", "achieved": ach,
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                           "traffic": None, "alg_flops_per_launch": f}
+    res["block"] = {
+        "hbm_gbps_alg": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "tflops_alg": (flops_attn + flops_score) / (ms_step * 1e-3) / 1e12,
+        "alg_bytes_per_step": step_bytes,
+        "alg_flops_per_step": flops_attn + flops_score,
+    }
+    res["kernels_ms"] = kern
+    res["sparse_layer_gbps_alg"] = (attended * KV_ROW_BYTES + nq * QO_BYTES) / (
+        sparse_layer_ms * 1e-3) / 1e9 if spec.n_sparse else None
+    if bridge is not None:
+        bf = 2 * 1048576 * 2048 * 256 * 3
+        res["bridging"] = {"ms": kern["bridge_gemm"], "tflops": bf / (kern["bridge_gemm"] * 1e-3) / 1e12,
+                           "frac_mfma": bf / (kern["bridge_gemm"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    res["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample (cpu baseline)")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -172,6 +172,23 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
                            int32_t window, int32_t top_k, float scale, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Kernel timing hook, for benchmarks and profilers that need per-kernel durations on the
+ * library's own stream (not an operation of the method). While attached, every hs2_*
+ * compute call records events[2*j] right before and events[2*j+1] right after its
+ * kernel of pipeline slot j (j < n_pairs), on that call's stream. Slots:
+ *   hs2_full_attn_select: 0 attention, 1 split combine, 2 score pass, 3 top-k filter,
+ *                         4 top-k finish
+ *   hs2_sparse_attn:      0 attention, 1 split combine
+ *   hs2_bridge_kv:        0 weight transpose, 1 fan-out GEMM
+ * A slot whose kernel a call does not need (e.g. no split combine when one workgroup
+ * covers a query) is not recorded. The events are hipEvent_t handles created and owned
+ * by the caller and must stay valid while attached. events == NULL or n_pairs == 0
+ * detaches. Process-wide and not synchronised: attach and detach only while no other
+ * thread calls the library. 0 <= n_pairs <= 16.
+ * ------------------------------------------------------------------------------------ */
+hs2_status hs2_set_kernel_events(void* const* events, int32_t n_pairs);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -140,17 +140,19 @@ __global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeArgs a) {
 
 }  // namespace
 
-hipError_t launch_bridge(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats, uint16_t* wt,
-                         hipStream_t s) {
+hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats, uint16_t* wt,
+                                   hipStream_t s) {
   WPtrs wp{};
   for (int m = 0; m < n_mats; ++m) wp.w[m] = w[m];
   hipLaunchKernelGGL(transpose_w_kernel, dim3(a.d_model / 64, kDim / 64, n_mats), dim3(256), 0, s, wp,
                      wt, a.d_model);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_rows == 0) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s) {
   const int64_t n_rt = (a.n_rows + kBM - 1) / kBM;
   const int64_t per_xcd = (n_rt + kXcds - 1) / kXcds;
-  const int64_t grid = per_xcd * kXcds * (n_mats / 2);
+  const int64_t grid = per_xcd * kXcds * (a.n_mats / 2);
   hipLaunchKernelGGL(bridge_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

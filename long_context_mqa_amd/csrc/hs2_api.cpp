@@ -158,6 +158,23 @@ SeqsDev to_dev(const hs2_seqs* b) {
   return d;
 }
 
+// Kernel timing hook state (see hs2_set_kernel_events).
+constexpr int kMaxEventPairs = 16;
+hipEvent_t g_events[2 * kMaxEventPairs];
+int g_event_pairs = 0;
+
+// Brackets the kernel of pipeline slot j of one entry-point call with the attached events.
+struct LaunchMarks {
+  hipStream_t s;
+  explicit LaunchMarks(hipStream_t st) : s(st) {}
+  hipError_t before(int j) const {
+    return j < g_event_pairs ? hipEventRecord(g_events[2 * j], s) : hipSuccess;
+  }
+  hipError_t after(int j) const {
+    return j < g_event_pairs ? hipEventRecord(g_events[2 * j + 1], s) : hipSuccess;
+  }
+};
+
 hs2_status hip_fail(hipError_t e, const char* what) {
   return fail(HS2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -172,6 +189,20 @@ T* at(void* ws, size_t off) {
 extern "C" {
 
 int32_t hs2_version(void) { return HS2_VERSION; }
+
+hs2_status hs2_set_kernel_events(void* const* events, int32_t n_pairs) {
+  if (n_pairs < 0 || n_pairs > kMaxEventPairs)
+    return fail(HS2_ERR_INVALID_ARG, "n_pairs must be in [0, %d] (got %d)", kMaxEventPairs, n_pairs);
+  if (!events || n_pairs == 0) {
+    g_event_pairs = 0;
+    return ok();
+  }
+  for (int i = 0; i < 2 * n_pairs; ++i)
+    if (!events[i]) return fail(HS2_ERR_INVALID_ARG, "event %d is NULL", i);
+  for (int i = 0; i < 2 * n_pairs; ++i) g_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_event_pairs = n_pairs;
+  return ok();
+}
 
 const char* hs2_last_error(void) { return g_err.c_str(); }
 
@@ -225,8 +256,11 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
   a.lse = lse;
   a.lse2 = lse2;
   const int grid = tq * p.attn.n_split;
-  hipError_t e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s)
-                     : launch_attn_bf16(a, false, grid, hist, counters, s);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess)
+    e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s) : launch_attn_bf16(a, false, grid, hist, counters, s);
+  if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "full attention launch");
   if (p.attn.n_split > 1) {
     CombineArgs c{};
@@ -242,7 +276,9 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     c.lse2 = lse2;
     c.hist = hist;
     c.counters = counters;
-    e = launch_combine(c, f32, s);
+    e = mk.before(1);
+    if (e == hipSuccess) e = launch_combine(c, f32, s);
+    if (e == hipSuccess) e = mk.after(1);
     if (e != hipSuccess) return hip_fail(e, "split combine launch");
   }
   TopkArgs tk{};
@@ -273,11 +309,19 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     sc.score_stride = p.score_stride;
     sc.scores = at<float>(workspace, p.off_scores);
     sc.hist = hist;
-    e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+    e = mk.before(2);
+    if (e == hipSuccess) e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+    if (e == hipSuccess) e = mk.after(2);
     if (e != hipSuccess) return hip_fail(e, "score launch");
+    e = mk.before(3);
+    if (e == hipSuccess) e = launch_topk_filter(tk, s);
+    if (e == hipSuccess) e = mk.after(3);
+    if (e != hipSuccess) return hip_fail(e, "top-k filter launch");
   }
-  e = launch_topk(tk, s);
-  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  e = mk.before(4);
+  if (e == hipSuccess) e = launch_topk_finish(tk, s);
+  if (e == hipSuccess) e = mk.after(4);
+  if (e != hipSuccess) return hip_fail(e, "top-k finish launch");
   return ok();
 }
 
@@ -324,8 +368,11 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
   a.lse = lse;
   a.lse2 = nullptr;
   const int grid = batch->total_q * p.attn.n_split;
-  hipError_t e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
-                     : launch_attn_bf16(a, true, grid, nullptr, nullptr, s);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess)
+    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s) : launch_attn_bf16(a, true, grid, nullptr, nullptr, s);
+  if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   if (p.attn.n_split > 1) {
     CombineArgs c{};
@@ -341,7 +388,9 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
     c.lse2 = nullptr;
     c.hist = nullptr;
     c.counters = nullptr;
-    e = launch_combine(c, f32, s);
+    e = mk.before(1);
+    if (e == hipSuccess) e = launch_combine(c, f32, s);
+    if (e == hipSuccess) e = mk.after(1);
     if (e != hipSuccess) return hip_fail(e, "split combine launch");
   }
   return ok();
@@ -387,7 +436,16 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
   a.n_rows = n_rows;
   a.d_model = d_model;
   a.n_mats = 2 * n_layers;
-  hipError_t e = launch_bridge(a, w, 2 * n_layers, static_cast<uint16_t*>(workspace), static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess) e = launch_bridge_transpose(a, w, 2 * n_layers, static_cast<uint16_t*>(workspace), s);
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "bridging weight transpose launch");
+  if (n_rows == 0) return ok();
+  e = mk.before(1);
+  if (e == hipSuccess) e = launch_bridge_gemm(a, s);
+  if (e == hipSuccess) e = mk.after(1);
   if (e != hipSuccess) return hip_fail(e, "bridging launch");
   return ok();
 }

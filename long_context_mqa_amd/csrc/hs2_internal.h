@@ -146,8 +146,10 @@ hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* h
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
 hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-hipError_t launch_bridge(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats,
-                         uint16_t* wt, hipStream_t s);
+hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s);
+hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats,
+                                   uint16_t* wt, hipStream_t s);
+hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s);
 
 }  // namespace hs2

@@ -287,12 +287,12 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.top_k > 0) {
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(a.b.total_q * a.n_split), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(topk_filter_kernel, dim3(a.b.total_q * a.n_split), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(topk_finish_kernel, dim3(a.b.total_q), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

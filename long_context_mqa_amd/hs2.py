@@ -28,6 +28,7 @@ EXPORTED = [
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
     "hs2_sparse_attn",
+    "hs2_set_kernel_events",
 ]
 
 
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_sparse_attn.restype = I32
     lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    lib.hs2_set_kernel_events.restype = I32
+    lib.hs2_set_kernel_events.argtypes = [P, I32]
     _lib = lib
     return lib
 
@@ -230,3 +233,16 @@ def bridge_kv(hidden, w_k: list, w_v: list, k_out: list | None = None, v_out: li
     _check(lib.hs2_bridge_kv(_ptr(hidden), n_rows, d_model, L, wk, wv, ko, vo, head_dim, _ptr(workspace),
                              workspace.numel(), _dtype_code(hidden), _stream(stream)))
     return k_out, v_out
+
+
+def set_kernel_events(events: list | None) -> None:
+    """hs2_set_kernel_events: bracket each kernel of later calls with HIP events.
+
+    `events` is a flat list of hipEvent_t handles (ints), two per kernel, or None."""
+    lib = load()
+    if not events:
+        _check(lib.hs2_set_kernel_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    set_kernel_events._keep = arr
+    _check(lib.hs2_set_kernel_events(arr, len(events) // 2))
