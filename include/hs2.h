@@ -46,7 +46,7 @@
  *     the given buffers is touched.
  *   - Supported shapes: n_heads == 64, head_dim == 128 (the MQA layout of the pages,
  *     [arex] "Numbers computed on three 80B-A3B models"); anything else returns
- *     HS2_ERR_UNSUPPORTED. 1 <= window <= 1<<20, 0 <= top_k <= HS2_MAX_TOP_K.
+ *     HS2_ERR_UNSUPPORTED. 1 <= window <= 1<<18, 0 <= top_k <= HS2_MAX_TOP_K.
  *   - Sequence lengths up to 2^31-1 rows; total rows up to 2^62.
  */
 #ifndef HS2_H_

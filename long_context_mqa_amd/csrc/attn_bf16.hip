@@ -36,9 +36,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kVRow = kDim + 8;     // padded LDS row (bf16 elements) of a V tile
-constexpr float kNegBig = -1.0e30f; // "no key yet" reference: exp2(x - kNegBig) never used
+constexpr float kNegBig = -1.0e30f; // "no key yet" reference
 constexpr float kLazy = 8.0f;       // reference moves only when exceeded by more than this
+constexpr int kTileBytes = kTile * kDim * 2;  // 8 KB: one K or V tile
+constexpr int kStages = 2;                    // per-wave LDS stages (K + V each)
+constexpr int kDmaPerHalf = kTileBytes / 1024;     // 8 wave-wide 16-byte loads per K or V tile
 
 __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -46,12 +48,39 @@ __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane l's
+// bytes land at LDS address `lds` + 16*l. Issued as asm so that the wait for it can be
+// placed by hand (s_waitcnt vmcnt); it has no register outputs.
+__device__ inline void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+// Tile layouts in LDS (32 rows of 256 bytes, filled by row-coalesced DMA):
+//  K: the 16-byte chunk c of row r is stored at chunk position c ^ (r & 15), so that the
+//     MFMA-operand reads (32 rows, same chunk) are free of bank conflicts;
+//  V: plain row-major, so that all V^T operand reads of a lane share one base address
+//     and differ by immediate offsets.
+__device__ inline uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4));
+}
+
 // Logical key list of one query. Full mode: positions 0..t. Gather mode: top_k selected
 // slots (entries outside the candidate range are masked) followed by the window rows.
 struct KeyList {
-  const int32_t* sel_row;
+  const int32_t* sel_lds;  // gather mode: selected rows of slots [sel_k0, ...) in LDS
+  int sel_k0;
   int64_t base;
-  int t, window, top_k, n_keys, w_eff, cand_hi;
+  int t, top_k, n_keys, w_eff, cand_hi;
   bool gather;
 
   __device__ inline void row(int p, int& rel, bool& ok) const {
@@ -61,7 +90,7 @@ struct KeyList {
       return;
     }
     if (p < top_k) {
-      const int s = sel_row[p];
+      const int s = sel_lds[p - sel_k0];
       ok = s >= 0 && s <= cand_hi;
       rel = ok ? s : 0;
       return;
@@ -72,30 +101,26 @@ struct KeyList {
   }
 };
 
-struct TileRegs {
-  bf16x8 k[8];   // K half-row of key l%32 (dims (l/32)*64 + s*8 ..)
-  uint4 v[8];    // V piece r: key r*4 + l/16, dims (l%16)*8 .. +8
-  bool ok;       // key l%32 of the tile is attended
-};
-
-__device__ inline void load_tile(const KeyList& kl, const __bf16* __restrict__ kp,
-                                 const uint16_t* __restrict__ vp, int p0, int p1, int lane,
-                                 TileRegs& r) {
-  int rel;
+// Row of key (p0 + l%32) of a tile for lane l, and the mask of attended keys of the tile.
+__device__ inline uint32_t tile_rows(const KeyList& kl, int p0, int p1, int lane, int& rel) {
   bool ok;
   const int p = p0 + (lane & 31);
   kl.row(p, rel, ok);
   ok = ok && p < p1;
   if (!ok) rel = 0;
-  r.ok = ok;
-  const __bf16* krow = kp + (kl.base + rel) * kDim + (lane >> 5) * 64;
+  return (uint32_t)__ballot(ok);
+}
+
+// Enqueues the 32 rows of a K tile (swizzled) or a V tile (row-major) into LDS. `rel` is
+// the row of key l%32 held by lane l; earlier LDS reads of the stage must have completed.
+template <bool kSwizzle>
+__device__ inline void issue_rows(const __bf16* __restrict__ src, int64_t base, int rel, int lane, uint32_t lds) {
+  wait_lgkm0();
 #pragma unroll
-  for (int s = 0; s < 8; ++s) r.k[s] = *reinterpret_cast<const bf16x8*>(krow + s * 8);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int key = q * 4 + (lane >> 4);
-    const int vrel = __shfl(rel, key);
-    r.v[q] = *reinterpret_cast<const uint4*>(vp + (kl.base + vrel) * kDim + (lane & 15) * 8);
+  for (int r = 0; r < 8; ++r) {
+    const int row = r * 4 + (lane >> 4);
+    const int chunk = kSwizzle ? ((lane & 15) ^ (row & 15)) : (lane & 15);
+    dma16(src + (base + __shfl(rel, row)) * kDim + chunk * 8, lds + r * 1024);
   }
 }
 
@@ -106,23 +131,21 @@ struct WaveState {
   float l[2];       // this lane's share of the denominator
 };
 
-__device__ inline void process_tile(WaveState& st, const bf16x8 (&qop)[2][8], const TileRegs& r,
-                                    uint16_t* __restrict__ vl, float c2, int lane) {
-  // stage V tile in LDS (row-major, padded rows)
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    *reinterpret_cast<uint4*>(vl + (q * 4 + (lane >> 4)) * kVRow + (lane & 15) * 8) = r.v[q];
-
-  // S^T = K Q^T
+// One 32-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T. Q^T operands and the V
+// tile are read from LDS; the K operands were read already (its stage is reused).
+__device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ qs, const bf16x8 (&kop)[8],
+                                    const uint8_t* __restrict__ vt, uint32_t vm, float c2, int lane) {
   f32x16 acc[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     acc[nb] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[nb] = mfma(r.k[s], qop[nb][s], acc[nb]);
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 q = *reinterpret_cast<const bf16x8*>(qs + ((nb * 8 + s) * 64 + lane) * 16);
+      acc[nb] = mfma(kop[s], q, acc[nb]);
+    }
   }
 
-  const uint32_t vm = (uint32_t)__ballot(r.ok);
   const int hrow = 4 * (lane >> 5);
   float x[2][16];
 #pragma unroll
@@ -180,27 +203,46 @@ __device__ inline void process_tile(WaveState& st, const bf16x8 (&qop)[2][8], co
     st.l[nb] += lsum;
   }
 
-  // O^T += V^T P^T; A operand: lane l holds V[key][32*mb + l%32] for the 8 keys of its slots
+  // O^T += V^T P^T. A operand: lane l holds V[key][32*mb + l%32] for the 8 keys
+  // 16*ks + 8*(i/4) + 4*(l/32) + i%4 of its slots (row-major V tile: immediate offsets).
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(vt) + hrow * kDim + (lane & 31);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 va;
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int key = 16 * ks + 8 * (ii >> 2) + hrow + (ii & 3);
-        va[ii] = __builtin_bit_cast(__bf16, vl[key * kVRow + 32 * mb + (lane & 31)]);
-      }
+      for (int ii = 0; ii < 8; ++ii)
+        va[ii] = __builtin_bit_cast(__bf16, vb[(16 * ks + 8 * (ii >> 2) + (ii & 3)) * kDim + 32 * mb]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) st.o[nb][mb] = mfma(va, pb[nb][ks], st.o[nb][mb]);
     }
-  }
 }
 
-// Shared memory of the attention kernel: V tiles during the key loop, then the merge.
+// K A-operands of the 8 contraction steps from a swizzled K tile.
+__device__ inline void read_k(const uint8_t* __restrict__ kt, int lane, bf16x8 (&kop)[8]) {
+  const int row = lane & 31;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    kop[s] = *reinterpret_cast<const bf16x8*>(kt + tile_off(row, (lane >> 5) * 8 + s));
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in {0, 8, 16, 24}
+__device__ inline void wait_vmcnt_dyn(int n) {
+  if (n >= 24) wait_vmcnt<24>();
+  else if (n >= 16) wait_vmcnt<16>();
+  else if (n >= 8) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+}
+
+// Shared memory of the attention kernel: per-wave K and V stages during the key loop,
+// then the cross-wave merge; Q (in MFMA operand order) and the gathered row list stay
+// outside the union.
+constexpr int kSelMax = 2048;  // gathered slots per workgroup (the host caps the split)
+
 struct AttnSmem {
   union {
-    uint16_t v[kWaves][kTile * kVRow];
+    uint8_t stage[kWaves][kStages][2][kTileBytes];
     struct {
       float m[kWaves][kHeads];
       float l[kWaves][kHeads];
@@ -209,12 +251,14 @@ struct AttnSmem {
       float o[kDim][kHeads + 1];
     } mg;
   };
+  uint8_t q[kHeads * kDim * 2];
+  int32_t sel[kSelMax];
 };
 
 template <bool kGather>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hist,
                                                         uint32_t* counters) {
-  __shared__ AttnSmem sm;
+  __shared__ __align__(16) AttnSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int i = blockIdx.x / a.n_split;
@@ -241,10 +285,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
 
   KeyList kl;
   kl.gather = kGather;
-  kl.sel_row = kGather ? a.sel + (size_t)i * a.top_k : nullptr;
   kl.base = base;
   kl.t = t;
-  kl.window = a.window;
   kl.top_k = a.top_k;
   kl.n_keys = logical_keys(kGather, t, a.window, a.top_k);
   kl.w_eff = min(a.window, t + 1);
@@ -253,20 +295,26 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
   if (k0 >= kl.n_keys) return;  // empty split: the combine does not read it
   const int k1 = min(kl.n_keys, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
-
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v);
-
-  bf16x8 qop[2][8];
+  kl.sel_lds = sm.sel;
+  kl.sel_k0 = k0;
+  if (kGather) {
+    const int32_t* selr = a.sel + (size_t)i * a.top_k;
+    const int s1 = min(min(k1, a.top_k), k0 + kSelMax);
+    for (int p = k0 + threadIdx.x; p < s1; p += blockDim.x) sm.sel[p - k0] = selr[p];
+  }
+  // Q^T B-operands in LDS: 16-byte piece (nb, s, lane) = Q[32*nb + l%32][(l/32)*64 + 8*s ..]
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)i * kHeads * kDim;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qop[nb][s] = *reinterpret_cast<const bf16x8*>(qp + (32 * nb + (lane & 31)) * kDim +
-                                                      (lane >> 5) * 64 + s * 8);
+    for (int e = threadIdx.x; e < 16 * 64; e += blockDim.x) {
+      const int ln = e & 63, sidx = (e >> 6) & 7, nb = e >> 9;
+      *reinterpret_cast<uint4*>(sm.q + e * 16) = *reinterpret_cast<const uint4*>(
+          qp + (32 * nb + (ln & 31)) * kDim + (ln >> 5) * 64 + sidx * 8);
+    }
   }
+  __syncthreads();
+
+  const __bf16* kp = static_cast<const __bf16*>(a.k);
+  const __bf16* vp = static_cast<const __bf16*>(a.v);
 
   WaveState st;
 #pragma unroll
@@ -277,21 +325,46 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
     for (int mb = 0; mb < 4; ++mb) st.o[nb][mb] = f32x16{};
   }
 
-  uint16_t* vl = sm.v[wave];
-  int tau = wave;
-  TileRegs cur, nxt;
-  if (tau < ntiles) load_tile(kl, kp, vp, k0 + tau * kTile, k1, lane, nxt);
-  for (; tau < ntiles; tau += kWaves) {
-    cur = nxt;
-    if (tau + kWaves < ntiles) load_tile(kl, kp, vp, k0 + (tau + kWaves) * kTile, k1, lane, nxt);
-    process_tile(st, qop, cur, vl, a.c2, lane);
+  // Tiles of this wave: wave, wave + 4, ...  Two LDS stages each for K and V. DMA groups
+  // are issued in the order K0 V0 K1 V1, then per iteration K(it+2) right after the K
+  // operands of tile it are in registers and V(it+2) after its PV step, so two tiles
+  // stream in while one is computed. Waits count the 8-load groups issued later.
+  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  uint32_t lk[kStages], lv[kStages];
+#pragma unroll
+  for (int sidx = 0; sidx < kStages; ++sidx) {
+    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][0]);
+    lv[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][1]);
+  }
+  uint32_t okm[kStages] = {0u, 0u};
+  int relv[kStages] = {0, 0};
+  for (int it = 0; it < min(ntw, kStages); ++it) {
+    okm[it] = tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, relv[it]);
+    issue_rows<true>(kp, base, relv[it], lane, lk[it]);
+    issue_rows<false>(vp, base, relv[it], lane, lv[it]);
+  }
+  for (int it = 0; it < ntw; ++it) {
+    const int sidx = it & 1;
+    const bool more1 = it + 1 < ntw, more2 = it + 2 < ntw;
+    wait_vmcnt_dyn(more1 ? 24 : 8);            // K(it) has landed
+    bf16x8 kop[8];
+    read_k(sm.stage[wave][sidx][0], lane, kop);
+    const uint32_t vm = okm[sidx];
+    int rel2 = 0;
+    if (more2) {
+      okm[sidx] = tile_rows(kl, k0 + (wave + (it + 2) * kWaves) * kTile, k1, lane, rel2);
+      issue_rows<true>(kp, base, rel2, lane, lk[sidx]);
+    }
+    wait_vmcnt_dyn((more1 ? 16 : 0) + (more2 ? 8 : 0));   // V(it) has landed
+    process_tile(st, sm.q, kop, sm.stage[wave][sidx][1], vm, a.c2, lane);
+    if (more2) issue_rows<false>(vp, base, rel2, lane, lv[sidx]);
   }
 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) st.l[nb] += __shfl_xor(st.l[nb], 32);
 
   // ---- merge the four waves (fixed order, deterministic) ----
-  __syncthreads();  // V tiles no longer needed
+  __syncthreads();  // LDS stages no longer needed
   if (lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -366,70 +439,110 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
 // ------------------------------------------------------------------------------------
 // Split combine: merges the partials of a query in split order, writes O, LSE and the
 // log2-domain LSE used by the score pass, and clears the query's selection counters.
+// Grid: total_q x kCombineSlabs; a slab covers 16 dims x 64 heads of the output.
 // ------------------------------------------------------------------------------------
+constexpr int kCombineSlabs = kDim / 16;
+constexpr int kMaxSplit = 256;
+
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int kMaxSplit = 256;
   __shared__ float w_s[kMaxSplit][kHeads];
-  __shared__ float fl[kHeads];
-  __shared__ float ob[kDim][kHeads + 1];
-  const int i = blockIdx.x;
+  __shared__ float red[4][kHeads];
+  __shared__ float fm[kHeads], fl[kHeads];
+  const int i = blockIdx.x / kCombineSlabs;
+  const int slab = blockIdx.x - i * kCombineSlabs;
+  const int tid = threadIdx.x;
+  const int h = tid & 63, grp = tid >> 6;
   if (a.hist) {
-    for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) a.hist[(size_t)i * kHistBins + e] = 0u;
-    if (threadIdx.x < 4) a.counters[(size_t)i * 4 + threadIdx.x] = 0u;
+    constexpr int per = kHistBins / kCombineSlabs;
+    for (int e = tid; e < per; e += blockDim.x) a.hist[(size_t)i * kHistBins + slab * per + e] = 0u;
+    if (slab == 0 && tid < 4) a.counters[(size_t)i * 4 + tid] = 0u;
   }
   int64_t base;
   int t;
   const bool valid = query_desc(a.b, i, base, t);
   OutT* out = static_cast<OutT*>(a.out) + (size_t)i * kHeads * kDim;
+  const int d0 = slab * 16 + grp * 4;
   if (!valid) {
-    for (int e = threadIdx.x; e < kHeads * kDim; e += blockDim.x) out[e] = (OutT)NAN;
-    if (threadIdx.x < kHeads) {
-      if (a.lse) a.lse[(size_t)i * kHeads + threadIdx.x] = NAN;
-      if (a.lse2) a.lse2[(size_t)i * kHeads + threadIdx.x] = NAN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)NAN;
+    if (slab == 0 && tid < kHeads) {
+      if (a.lse) a.lse[(size_t)i * kHeads + tid] = NAN;
+      if (a.lse2) a.lse2[(size_t)i * kHeads + tid] = NAN;
     }
     return;
   }
   const int n_keys = logical_keys(a.gather != 0, t, a.window, a.top_k);
   const int nv = min(a.n_split, (n_keys + a.split_keys - 1) / a.split_keys);
   const Partial* P = a.part + (size_t)i * a.n_split;
-  if (threadIdx.x < kHeads) {
-    const int h = threadIdx.x;
-    float M = P[0].m[h];
-    for (int s = 1; s < nv; ++s) M = fmaxf(M, P[s].m[h]);
-    float L = 0.0f;
-    for (int s = 0; s < nv; ++s) {
-      const float w = __builtin_amdgcn_exp2f(P[s].m[h] - M);
-      w_s[s][h] = w;
-      L += P[s].l[h] * w;
-    }
+  // max over splits: four groups of 64 threads take every fourth split
+  float mx = -INFINITY;
+  for (int s2 = grp; s2 < nv; s2 += 4) mx = fmaxf(mx, P[s2].m[h]);
+  red[grp][h] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int s2 = grp; s2 < nv; s2 += 4) {
+    const float w = __builtin_amdgcn_exp2f(P[s2].m[h] - M);
+    w_s[s2][h] = w;
+    lsum += P[s2].l[h] * w;
+  }
+  red[grp][h] = lsum;
+  __syncthreads();
+  if (tid < kHeads) {
+    const float L = (red[0][h] + red[1][h]) + (red[2][h] + red[3][h]);
+    fm[h] = M;
     fl[h] = L;
-    const float l2 = M + __log2f(L);
-    if (a.lse) a.lse[(size_t)i * kHeads + h] = l2 * kLn2;
-    if (a.lse2) a.lse2[(size_t)i * kHeads + h] = l2;
+    if (slab == 0) {
+      const float l2 = M + __log2f(L);
+      if (a.lse) a.lse[(size_t)i * kHeads + h] = l2 * kLn2;
+      if (a.lse2) a.lse2[(size_t)i * kHeads + h] = l2;
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < kHeads * kDim; e += blockDim.x) {
-    const int d = e >> 6, h = e & 63;
-    float acc = 0.0f;
-    for (int s = 0; s < nv; ++s) acc += P[s].o[e] * w_s[s][h];
-    ob[d][h] = acc;
+  // thread (h, grp): dims d0 .. d0+3 of head h; loads of 4 splits in flight at a time
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int s2 = 0;
+  for (; s2 + 4 <= nv; s2 += 4) {
+    float v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[u][r] = P[s2 + u].o[(d0 + r) * kHeads + h];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = w_s[s2 + u][h];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += v[u][r] * w;
+    }
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kHeads * kDim; e += blockDim.x) {
-    const int h = e >> 7, d = e & 127;
-    out[e] = (OutT)(ob[d][h] / fl[h]);
+  for (; s2 < nv; ++s2) {
+    const float w = w_s[s2][h];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += P[s2].o[(d0 + r) * kHeads + h] * w;
   }
+  const float inv = 1.0f / fl[h];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)(acc[r] * inv);
 }
 
 // ------------------------------------------------------------------------------------
 // Selection score pass: score_j = sum_h exp2(x_hj - lse2_h) for candidates j <= t-window,
 // written per query, plus a histogram of the first radix digit (bits 30..19).
 // S = Q K^T here (heads as rows): each lane sums its 32 head values of one key, and one
-// exchange with lane l^32 completes the 64-head sum.
+// exchange with lane l^32 completes the 64-head sum. K tiles stream through kScoreStages
+// per-wave LDS stages (same swizzled layout and DMA as pass 1).
 // ------------------------------------------------------------------------------------
+constexpr int kScoreStages = 4;
+
+struct ScoreSmem {
+  uint8_t stage[kWaves][kScoreStages][kTileBytes];
+  uint32_t hist[kHistBins];
+};
+
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
-  __shared__ uint32_t hist_s[kHistBins];
+  __shared__ __align__(16) ScoreSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int i = blockIdx.x / a.n_split;
@@ -444,7 +557,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
   const int k1 = min(nc, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
 
-  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) hist_s[e] = 0u;
+  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) sm.hist[e] = 0u;
 
   bf16x8 qop[2][8];
   {
@@ -463,24 +576,30 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       l2[mb][j] = a.lse2[(size_t)i * kHeads + 32 * mb + 8 * (j >> 2) + hrow + (j & 3)];
-  __syncthreads();
+  __syncthreads();  // histogram cleared; the loads above have completed
 
   const __bf16* kp = static_cast<const __bf16*>(a.k);
   float* srow = a.scores + (size_t)i * a.score_stride;
-  bf16x8 kc[8], kn[8];
-  auto load = [&](int tau, bf16x8 (&kr)[8]) {
-    const int p = k0 + tau * kTile + (lane & 31);
+  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  uint32_t lk[kScoreStages];
+#pragma unroll
+  for (int sidx = 0; sidx < kScoreStages; ++sidx)
+    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx]);
+  auto issue = [&](int it, uint32_t lds) {
+    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
     const int rel = p < k1 ? p : 0;
-    const __bf16* krow = kp + (base + rel) * kDim + (lane >> 5) * 64;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kr[s] = *reinterpret_cast<const bf16x8*>(krow + s * 8);
+    issue_rows<true>(kp, base, rel, lane, lds);
   };
-  int tau = wave;
-  if (tau < ntiles) load(tau, kn);
-  for (; tau < ntiles; tau += kWaves) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kc[s] = kn[s];
-    if (tau + kWaves < ntiles) load(tau + kWaves, kn);
+  for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, lk[it]);
+  for (int it = 0; it < ntw; ++it) {
+    const int sidx = it % kScoreStages;
+    // K(it) has landed once at most the groups issued after it are outstanding (score
+    // stores issued meanwhile only make this wait longer, never shorter)
+    const int later = min(ntw, it + kScoreStages) - (it + 1);
+    wait_vmcnt_dyn(later * kDmaPerHalf);
+    bf16x8 kc[8];
+    read_k(sm.stage[wave][sidx], lane, kc);
+    if (it + kScoreStages < ntw) issue(it + kScoreStages, lk[sidx]);
     f32x16 acc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -496,16 +615,16 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
     // lane l and l^32 hold complementary heads of the same key; add in a fixed order
     const float other = __shfl_xor(sum, 32);
     const float total = (lane < 32) ? sum + other : other + sum;
-    const int p = k0 + tau * kTile + (lane & 31);
+    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
     if (lane < 32 && p < k1) {
       srow[p] = total;
-      atomicAdd(&hist_s[__float_as_uint(total) >> kHistShift], 1u);
+      atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
     }
   }
   __syncthreads();
   uint32_t* hq = a.hist + (size_t)i * kHistBins;
   for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) {
-    const uint32_t c = hist_s[e];
+    const uint32_t c = sm.hist[e];
     if (c) atomicAdd(&hq[e], c);
   }
 }
@@ -522,10 +641,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, bool gather, int grid, uint32_t* 
 }
 
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s) {
+  const dim3 grid(a.b.total_q * kCombineSlabs);
   if (f32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(a.b.total_q), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(a.b.total_q), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

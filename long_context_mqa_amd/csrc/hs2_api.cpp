@@ -32,9 +32,10 @@ hs2_status ok() {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetGroups = 512;  // attention workgroups per launch (2 per CU)
+constexpr int kTargetGroups = 256;  // workgroups per launch: one per CU
 constexpr int kMaxSplit = 256;      // bound of the split combine
-constexpr int kFilterLen = 16384;   // candidates per top-k filter workgroup
+constexpr int kSparseSplitMax = 2048;  // keys per sparse workgroup (LDS row list)
+constexpr int kFilterLen = 8192;    // candidates per top-k filter workgroup (256 threads x 32)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -46,16 +47,26 @@ struct Split {
 };
 
 // Splits the logical key range [0, max_keys) of each query over workgroups so that the
-// launch has about kTargetGroups workgroups; each split is a multiple of 4 waves x 32.
-Split plan_split(int total_q, int64_t max_keys) {
-  const int unit = kTile * kWaves;
+// launch fills the GPU once (kTargetGroups workgroups of work, one per CU at the LDS
+// size of the attention and score kernels). `work` estimates the keys of the whole
+// launch; splits are multiples of one 32-key tile. Workgroups beyond a query's own
+// range exit at once.
+Split plan_split(int64_t work, int64_t max_keys) {
   Split s;
-  if (max_keys <= 0) return Split{1, unit};
-  int want = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(kTargetGroups, std::max(1, total_q))));
-  want = (int)std::min<int64_t>(want, ceil_div(max_keys, unit));
-  s.split_keys = (int)(ceil_div(ceil_div(max_keys, want), unit) * unit);
+  if (max_keys <= 0) return Split{1, kTile};
+  int64_t keys = std::max<int64_t>(ceil_div(std::max<int64_t>(work, 1), kTargetGroups), ceil_div(max_keys, kMaxSplit));
+  keys = ceil_div(keys, kTile) * kTile;
+  s.split_keys = (int)std::min<int64_t>(keys, ceil_div(max_keys, kTile) * kTile);
   s.n_split = (int)ceil_div(max_keys, s.split_keys);
   return s;
+}
+
+// Keys processed by one launch: every query over up to max_keys, bounded for ragged
+// single-query sequences by the rows of the batch.
+int64_t launch_work(const hs2_seqs* b, int64_t max_keys) {
+  const int64_t tq = std::max(0, b->total_q);
+  const int64_t by_rows = b->total_kv_rows * std::max(1, b->max_q_per_seq);
+  return std::min(tq * max_keys, std::max<int64_t>(by_rows, max_keys));
 }
 
 struct SelectPlan {
@@ -69,9 +80,9 @@ struct SelectPlan {
 SelectPlan plan_select(const hs2_seqs* b, int window, int top_k) {
   SelectPlan p;
   const int64_t tq = std::max(0, b->total_q);
-  p.attn = plan_split((int)tq, b->max_kv_len);
+  p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
   const int64_t max_cand = std::max<int64_t>(0, (int64_t)b->max_kv_len - window + 1);
-  p.score = plan_split((int)tq, max_cand);
+  p.score = plan_split(launch_work(b, max_cand), max_cand);
   p.f_split = (int)std::max<int64_t>(1, ceil_div(max_cand, kFilterLen));
   p.score_stride = (max_cand + 63) / 64 * 64;
   size_t off = 0;
@@ -104,7 +115,11 @@ SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k) {
   SparsePlan p;
   const int64_t tq = std::max(0, b->total_q);
   const int64_t max_keys = (int64_t)top_k + std::min<int64_t>(window, b->max_kv_len);
-  p.attn = plan_split((int)tq, max_keys);
+  p.attn = plan_split(tq * max_keys, max_keys);
+  if (p.attn.split_keys > kSparseSplitMax) {  // gathered slots of a workgroup are staged in LDS
+    p.attn.split_keys = kSparseSplitMax;
+    p.attn.n_split = (int)ceil_div(max_keys, kSparseSplitMax);
+  }
   p.total = p.attn.n_split > 1 ? align_up((size_t)tq * p.attn.n_split * sizeof(Partial)) : 0;
   return p;
 }
@@ -133,7 +148,7 @@ hs2_status check_attn_common(const hs2_seqs* b, const void* q, const void* k, co
   if (n_heads != kHeads || head_dim != kDim)
     return fail(HS2_ERR_UNSUPPORTED, "only n_heads=64, head_dim=128 are supported (got %d, %d)", n_heads,
                 head_dim);
-  if (window < 1 || window > (1 << 20)) return fail(HS2_ERR_INVALID_ARG, "window must be in [1, 2^20] (got %d)", window);
+  if (window < 1 || window > (1 << 18)) return fail(HS2_ERR_INVALID_ARG, "window must be in [1, 2^18] (got %d)", window);
   if (top_k < 0 || top_k > HS2_MAX_TOP_K)
     return fail(HS2_ERR_INVALID_ARG, "top_k must be in [0, %d] (got %d)", HS2_MAX_TOP_K, top_k);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(HS2_ERR_INVALID_ARG, "scale must be finite and > 0");

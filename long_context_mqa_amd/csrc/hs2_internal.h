@@ -17,7 +17,7 @@ constexpr int kWaves = 4;      // waves per attention workgroup
 constexpr int kHistBits = 12;  // first radix digit: bits 30..19 of a non-negative fp32 score
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 31 - kHistBits;
-constexpr int kCandCap = 8192; // threshold-bin candidates kept per query for the in-LDS select
+constexpr int kCandCap = 4096; // threshold-bin candidates kept per query for the in-LDS select
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -114,12 +114,19 @@ struct BridgeArgs {
 };
 
 // Resolves query i: sequence row base and position t. Returns false when the
-// descriptor is inconsistent (the query is then not computed).
+// descriptor is inconsistent (the query is then not computed). The sequence is first
+// guessed proportionally (exact for batches with equal query counts per sequence), and
+// found by binary search over q_start otherwise.
 __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t) {
-  int lo = 0, hi = b.num_seqs - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (b.q_start[mid] <= i) lo = mid; else hi = mid - 1;
+  int lo = (int)(((int64_t)i * b.num_seqs) / max(1, b.total_q));
+  if (lo >= b.num_seqs) lo = b.num_seqs - 1;
+  if (!(b.q_start[lo] <= i && i < b.q_start[lo + 1])) {
+    lo = 0;
+    int hi = b.num_seqs - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (b.q_start[mid] <= i) lo = mid; else hi = mid - 1;
+    }
   }
   base = b.kv_start[lo];
   const int n = b.kv_len[lo];

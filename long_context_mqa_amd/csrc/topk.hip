@@ -11,13 +11,15 @@
 // order like the values; the 64-bit key ((bits << 32) | ~position) is then unique per
 // candidate and its k largest values are exactly the selection.
 //
-// Pipeline per query (the score pass already built a histogram of bits 30..19):
+// Two kernels (the score pass already built a histogram of bits 30..19 of every
+// candidate's score):
 //   filter  (many workgroups per query): from the histogram, find the bin b1 that holds
-//           the k-th largest; keys with a larger bin are selected outright, keys in b1
-//           are copied to a per-query candidate list (up to kCandCap).
+//           the k-th largest; keys of a chunk in a larger bin are selected outright, keys
+//           in b1 are copied to a per-query candidate list (up to kCandCap).
 //   finish  (one workgroup per query): radix-select the remaining r keys among the b1
 //           candidates in LDS (or, if b1 overflowed the list, by streaming the query's
-//           scores again), then sort the k positions ascending and write them.
+//           scores again), then order the k positions ascending and write them.
+//           Queries with at most k candidates take all of them.
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -87,79 +89,118 @@ __device__ inline void threshold_bin(const uint32_t* __restrict__ hist, int k, u
 
 __device__ inline int cand_count(int t, int window) { return max(0, t - window + 1); }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
-  __shared__ uint32_t s_wave[kThreads / 64];
-  __shared__ int s_res[2];
-  const int i = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - i * a.n_split;
-  int64_t base;
-  int t;
-  if (!query_desc(a.b, i, base, t)) return;
-  const int nc = cand_count(t, a.window);
-  if (a.top_k == 0 || nc <= a.top_k) return;
+// Filter: each thread takes kPerThread candidates (strided, coalesced), counts the ones
+// above the threshold bin and in it, and each wave reserves its output slots with one
+// atomic per list.
+constexpr int kPerThread = 32;
+
+__device__ void filter_chunk(const TopkArgs& a, int i, int nc, int split, uint32_t* s_wave, int* s_res,
+                             uint32_t* s_tot) {
   const int k0 = split * a.split_len;
   if (k0 >= nc) return;
   const int k1 = min(nc, k0 + a.split_len);
 
+  const float* sc = a.scores + (size_t)i * a.score_stride;
+  uint32_t u[kPerThread];
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int p = k0 + r * kThreads + threadIdx.x;
+    u[r] = p < k1 ? __float_as_uint(sc[p]) : 0u;
+  }
   int b1, above;
   threshold_bin(a.hist + (size_t)i * kHistBins, a.top_k, s_wave, s_res, b1, above);
 
-  const float* sc = a.scores + (size_t)i * a.score_stride;
-  uint32_t* cnt = a.counters + (size_t)i * 4;
+  uint32_t na = 0, nb = 0;
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int p = k0 + r * kThreads + threadIdx.x;
+    const int d = (int)(u[r] >> kHistShift);
+    na += (p < k1 && d > b1) ? 1u : 0u;
+    nb += (p < k1 && d == b1) ? 1u : 0u;
+  }
+  const uint32_t ia = wave_incl_scan(na), ib = wave_incl_scan(nb);
+  const int lane = threadIdx.x & 63;
+  // one atomic per workgroup and list: wave totals combined in LDS
+  const int wave = threadIdx.x >> 6;
+  if (lane == 63) {
+    s_tot[wave] = ia;
+    s_tot[kThreads / 64 + wave] = ib;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t ta = 0, tb = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      ta += s_tot[w];
+      tb += s_tot[kThreads / 64 + w];
+    }
+    s_tot[2 * (kThreads / 64)] = ta ? atomicAdd(&a.counters[(size_t)i * 4 + 0], ta) : 0u;
+    s_tot[2 * (kThreads / 64) + 1] = tb ? atomicAdd(&a.counters[(size_t)i * 4 + 1], tb) : 0u;
+  }
+  __syncthreads();
+  uint32_t oa = s_tot[2 * (kThreads / 64)] + ia - na;
+  uint32_t ob = s_tot[2 * (kThreads / 64) + 1] + ib - nb;
+  for (int w = 0; w < wave; ++w) {
+    oa += s_tot[w];
+    ob += s_tot[kThreads / 64 + w];
+  }
   int32_t* abv = a.above + (size_t)i * a.top_k;
   uint2* cand = a.cand + (size_t)i * kCandCap;
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int p0 = k0; p0 < k1; p0 += kThreads) {
-    const int p = p0 + threadIdx.x;
-    uint32_t u = 0;
-    int d = -1;
-    if (p < k1) {
-      u = __float_as_uint(sc[p]);
-      d = (int)(u >> kHistShift);
-    }
-    const bool is_above = d > b1;
-    const bool is_bin = d == b1;
-    const uint64_t ma = __ballot(is_above);
-    const uint64_t mb = __ballot(is_bin);
-    uint32_t base_a = 0, base_b = 0;
-    if (lane == 0) {
-      if (ma) base_a = atomicAdd(&cnt[0], (uint32_t)__popcll(ma));
-      if (mb) base_b = atomicAdd(&cnt[1], (uint32_t)__popcll(mb));
-    }
-    base_a = __shfl(base_a, 0);
-    base_b = __shfl(base_b, 0);
-    if (is_above) {
-      const uint32_t slot = base_a + (uint32_t)__popcll(ma & lt_mask);
-      if (slot < (uint32_t)a.top_k) abv[slot] = p;
-    } else if (is_bin) {
-      const uint32_t slot = base_b + (uint32_t)__popcll(mb & lt_mask);
-      if (slot < (uint32_t)kCandCap) cand[slot] = make_uint2(u, (uint32_t)p);
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int p = k0 + r * kThreads + threadIdx.x;
+    if (p >= k1) continue;
+    const int d = (int)(u[r] >> kHistShift);
+    if (d > b1) {
+      if (oa < (uint32_t)a.top_k) abv[oa] = p;
+      ++oa;
+    } else if (d == b1) {
+      if (ob < (uint32_t)kCandCap) cand[ob] = make_uint2(u[r], (uint32_t)p);
+      ++ob;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Radix select of the r largest 64-bit keys among the threshold-bin elements.
-// Key of an element: ((u & low bits) << 32) | ~position: 51 significant bits, resolved in
-// seven digit passes (8,8,8,8,8,8,3 bits). Exactly r elements have a key >= the result.
+// Selection inside the threshold bin. The r largest elements by (score bits, then
+// smaller position) are found by a radix select over the 19 score bits below the first
+// digit (passes of 11 and 8 bits); only if the last score value is shared by more
+// elements than still needed are positions resolved too (four 8-bit passes over ~p).
 constexpr int kSortCap = HS2_MAX_TOP_K;
+constexpr int kBuckets = 1024;
 constexpr uint32_t kLowMask = (1u << kHistShift) - 1u;
 
 struct SelShared {
-  uint32_t hist[256];
   uint32_t s_wave[kThreads / 64];
+  uint32_t tot[2 * (kThreads / 64) + 2];
   int res[4];
   uint32_t nsel;
   int32_t sel[kSortCap];
-  uint32_t cu[kCandCap];
-  uint32_t cp[kCandCap];
+  union {
+    struct {  // selection inside the threshold bin
+      uint32_t hist[2048];
+      uint32_t cu[kCandCap];
+      uint32_t cp[kCandCap];
+    };
+    struct {  // ordering of the selected positions
+      int32_t sorted[kSortCap];
+      uint32_t bcnt[kBuckets];
+      uint32_t bfill[kBuckets];
+      uint32_t bstart[kBuckets];
+    };
+  };
 };
-
-__device__ inline uint64_t sel_key(uint32_t u_low, uint32_t p) {
-  return ((uint64_t)u_low << 32) | (uint64_t)(~p);
-}
 
 // Visits the threshold-bin elements: from LDS (n elements) or by streaming the scores.
 template <bool kLds, typename F>
@@ -175,46 +216,185 @@ __device__ inline void for_each_elem(const SelShared& sh, uint32_t n, const floa
   }
 }
 
-template <bool kLds>
-__device__ void radix_select_append(SelShared& sh, uint32_t n, const float* __restrict__ sc, int nc,
-                                    int b1, int r_need) {
-  uint64_t prefix = 0;
-  int r_rem = r_need;
-  for (int pass = 0; pass < 7; ++pass) {
-    const int shift = pass < 6 ? 43 - 8 * pass : 0;
-    const int width = pass < 6 ? 8 : 3;
-    const int hi = shift + width;
-    for (int e = threadIdx.x; e < 256; e += kThreads) sh.hist[e] = 0u;
-    __syncthreads();
-    const uint64_t pre_hi = prefix >> hi;
-    for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t p) {
-      const uint64_t key = sel_key(ul, p);
-      if ((key >> hi) == pre_hi) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & ((1u << width) - 1u)], 1u);
-    });
-    __syncthreads();
-    const int bin = 255 - (int)threadIdx.x;
-    const uint32_t c = (bin < (1 << width)) ? sh.hist[bin] : 0u;
-    uint32_t total;
-    const uint32_t excl = block_excl_scan(c, sh.s_wave, total);
-    if (threadIdx.x == 0) { sh.res[0] = 0; sh.res[1] = 0; }
-    __syncthreads();
-    if (excl < (uint32_t)r_rem && (uint32_t)r_rem <= excl + c) {
-      sh.res[0] = bin;
-      sh.res[1] = (int)excl;
-    }
-    __syncthreads();
-    prefix |= (uint64_t)sh.res[0] << shift;
-    r_rem -= sh.res[1];
-    __syncthreads();
-  }
-  const uint64_t kstar = prefix;
+// One digit pass: histogram of digit (key >> shift) & (2^width - 1) over the elements
+// whose key matches `prefix` above the digit, then the digit value holding the r-th
+// largest and the count of larger elements. key(ul, p) is given by `key_of`.
+template <bool kLds, typename K>
+__device__ inline void digit_pass(SelShared& sh, uint32_t n, const float* __restrict__ sc, int nc, int b1,
+                                  K&& key_of, uint64_t prefix, int shift, int width, int r, int& digit,
+                                  int& larger) {
+  const int nbins = 1 << width;
+  for (int e = threadIdx.x; e < nbins; e += kThreads) sh.hist[e] = 0u;
+  __syncthreads();
+  const int hi = shift + width;
   for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t p) {
-    if (sel_key(ul, p) >= kstar) {
+    const uint64_t key = key_of(ul, p);
+    if ((key >> hi) == (prefix >> hi)) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+  });
+  __syncthreads();
+  // thread tid owns bins from the top: nbins / kThreads consecutive bins, descending
+  const int per = (nbins + kThreads - 1) / kThreads;
+  const int top = nbins - 1 - (int)threadIdx.x * per;
+  uint32_t tot = 0;
+  for (int q = 0; q < per; ++q)
+    if (top - q >= 0) tot += sh.hist[top - q];
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(tot, sh.s_wave, total);
+  if (threadIdx.x == 0) {
+    sh.res[0] = 0;
+    sh.res[1] = 0;
+  }
+  __syncthreads();
+  if (excl < (uint32_t)r && (uint32_t)r <= excl + tot) {
+    uint32_t run = excl;
+    for (int q = 0; q < per; ++q) {
+      if (top - q < 0) break;
+      const uint32_t c = sh.hist[top - q];
+      if (run < (uint32_t)r && (uint32_t)r <= run + c) {
+        sh.res[0] = top - q;
+        sh.res[1] = (int)run;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  digit = sh.res[0];
+  larger = sh.res[1];
+  __syncthreads();
+}
+
+template <bool kLds>
+__device__ void select_in_bin(SelShared& sh, uint32_t n, const float* __restrict__ sc, int nc, int b1,
+                              int r_need) {
+  auto score_key = [](uint32_t ul, uint32_t) { return (uint64_t)ul; };
+  uint64_t pre = 0;
+  int r = r_need, dg, lg;
+  digit_pass<kLds>(sh, n, sc, nc, b1, score_key, pre, 8, 11, r, dg, lg);
+  pre |= (uint64_t)dg << 8;
+  r -= lg;
+  digit_pass<kLds>(sh, n, sc, nc, b1, score_key, pre, 0, 8, r, dg, lg);
+  pre |= (uint64_t)dg;
+  r -= lg;
+  const uint32_t ustar = (uint32_t)pre;  // score bits of the r_need-th largest
+  // r elements with score bits == ustar are still needed; ties go to smaller positions
+  if (threadIdx.x == 0) sh.res[2] = 0;
+  __syncthreads();
+  for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t) {
+    if (ul == ustar) atomicAdd(&sh.res[2], 1);
+  });
+  __syncthreads();
+  const int n_eq = sh.res[2];
+  uint32_t pstar_inv = 0;  // ~position threshold among the ties (0: take them all)
+  if (n_eq > r) {
+    auto tie_key = [ustar](uint32_t ul, uint32_t p) {
+      return ul == ustar ? ((uint64_t)1 << 32) | (uint64_t)(~p) : (uint64_t)0;
+    };
+    uint64_t tp = (uint64_t)1 << 32;
+    int rr = r;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      digit_pass<kLds>(sh, n, sc, nc, b1, tie_key, tp, shift, 8, rr, dg, lg);
+      tp |= (uint64_t)dg << shift;
+      rr -= lg;
+    }
+    pstar_inv = (uint32_t)tp;
+  }
+  __syncthreads();
+  for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t p) {
+    const bool take = ul > ustar || (ul == ustar && (~p) >= pstar_inv);
+    if (take) {
       const uint32_t slot = atomicAdd(&sh.nsel, 1u);
       if (slot < (uint32_t)kSortCap) sh.sel[slot] = (int32_t)p;
     }
   });
   __syncthreads();
+}
+
+// Final selection of query i (nc > k): run by one workgroup after every filter chunk of
+// the query has been written.
+__device__ void finish_query(const TopkArgs& a, SelShared& sh, int i, int nc, int32_t* out) {
+  const int k = a.top_k;
+  const uint32_t* hq = a.hist + (size_t)i * kHistBins;
+  int b1, above;
+  threshold_bin(hq, k, sh.s_wave, sh.res, b1, above);
+  const int r_need = k - above;
+  const uint32_t n_bin = __builtin_nontemporal_load(&hq[b1]);
+  const int32_t* abv = a.above + (size_t)i * k;
+  for (int e = threadIdx.x; e < above; e += kThreads) sh.sel[e] = __builtin_nontemporal_load(&abv[e]);
+  if (threadIdx.x == 0) sh.nsel = (uint32_t)above;
+  const float* sc = a.scores + (size_t)i * a.score_stride;
+  if (n_bin <= (uint32_t)kCandCap) {
+    const uint2* cand = a.cand + (size_t)i * kCandCap;
+    for (uint32_t e = threadIdx.x; e < n_bin; e += kThreads) {
+      const uint32_t cx = __builtin_nontemporal_load(&cand[e].x);
+      const uint32_t cy = __builtin_nontemporal_load(&cand[e].y);
+      sh.cu[e] = cx & kLowMask;
+      sh.cp[e] = cy;
+    }
+    __syncthreads();
+    select_in_bin<true>(sh, n_bin, sc, nc, b1, r_need);
+  } else {
+    __syncthreads();
+    select_in_bin<false>(sh, 0, sc, nc, b1, r_need);
+  }
+  // ascending order: bucket by position (kBuckets equal ranges of [0, nc)), prefix sums,
+  // scatter, then the rank inside a bucket (buckets hold ~1 position on average)
+  for (int e = threadIdx.x; e < kBuckets; e += kThreads) {
+    sh.bcnt[e] = 0u;
+    sh.bfill[e] = 0u;
+  }
+  __syncthreads();
+  auto bucket = [nc](int32_t p) { return (int)(((int64_t)p * kBuckets) / nc); };
+  for (int e = threadIdx.x; e < k; e += kThreads) atomicAdd(&sh.bcnt[bucket(sh.sel[e])], 1u);
+  __syncthreads();
+  {
+    constexpr int per = kBuckets / kThreads;
+    uint32_t c[per], tot = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+      c[q] = sh.bcnt[threadIdx.x * per + q];
+      tot += c[q];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan(tot, sh.s_wave, total);
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+      sh.bstart[threadIdx.x * per + q] = run;
+      run += c[q];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < k; e += kThreads) {
+    const int32_t x = sh.sel[e];
+    const int bk = bucket(x);
+    sh.sorted[sh.bstart[bk] + atomicAdd(&sh.bfill[bk], 1u)] = x;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < k; e += kThreads) {
+    const int32_t x = sh.sorted[e];
+    const int bk = bucket(x);
+    const int b0 = (int)sh.bstart[bk], bn = (int)sh.bcnt[bk];
+    int rank = b0;
+    for (int f = b0; f < b0 + bn; ++f) rank += sh.sorted[f] < x ? 1 : 0;
+    sh.sel[rank] = x;
+  }
+  __syncthreads();
+  if (out)
+    for (int e = threadIdx.x; e < k; e += kThreads) out[e] = sh.sel[e];
+  if (a.sel_count && threadIdx.x == 0) a.sel_count[i] = k;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
+  __shared__ uint32_t s_wave[kThreads / 64];
+  __shared__ int s_res[4];
+  __shared__ uint32_t s_tot[2 * (kThreads / 64) + 2];
+  const int i = blockIdx.x / a.n_split;
+  const int split = blockIdx.x - i * a.n_split;
+  int64_t base;
+  int t;
+  if (!query_desc(a.b, i, base, t)) return;
+  const int nc = cand_count(t, a.window);
+  if (a.top_k == 0 || nc <= a.top_k) return;
+  filter_chunk(a, i, nc, split, s_wave, s_res, s_tot);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
@@ -223,66 +403,21 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
   int32_t* out = a.sel_idx ? a.sel_idx + (size_t)i * a.top_k : nullptr;
   int64_t base;
   int t;
+  const int k = a.top_k;
   if (!query_desc(a.b, i, base, t)) {
     if (out)
-      for (int e = threadIdx.x; e < a.top_k; e += kThreads) out[e] = -1;
+      for (int e = threadIdx.x; e < k; e += kThreads) out[e] = -1;
     if (a.sel_count && threadIdx.x == 0) a.sel_count[i] = -1;
     return;
   }
   const int nc = cand_count(t, a.window);
-  const int k = a.top_k;
   if (k == 0 || nc <= k) {
     if (out)
       for (int e = threadIdx.x; e < k; e += kThreads) out[e] = e < nc ? e : -1;
     if (a.sel_count && threadIdx.x == 0) a.sel_count[i] = min(nc, k);
     return;
   }
-  const uint32_t* hq = a.hist + (size_t)i * kHistBins;
-  int b1, above;
-  threshold_bin(hq, k, sh.s_wave, sh.res, b1, above);
-  const int r_need = k - above;
-  const uint32_t n_bin = hq[b1];
-  const int32_t* abv = a.above + (size_t)i * k;
-  for (int e = threadIdx.x; e < above; e += kThreads) sh.sel[e] = abv[e];
-  if (threadIdx.x == 0) sh.nsel = (uint32_t)above;
-  const float* sc = a.scores + (size_t)i * a.score_stride;
-  if (n_bin <= (uint32_t)kCandCap) {
-    const uint2* cand = a.cand + (size_t)i * kCandCap;
-    for (uint32_t e = threadIdx.x; e < n_bin; e += kThreads) {
-      const uint2 c = cand[e];
-      sh.cu[e] = c.x & kLowMask;
-      sh.cp[e] = c.y;
-    }
-    __syncthreads();
-    radix_select_append<true>(sh, n_bin, sc, nc, b1, r_need);
-  } else {
-    __syncthreads();
-    radix_select_append<false>(sh, 0, sc, nc, b1, r_need);
-  }
-  // bitonic sort of the k positions, ascending (padded to a power of two)
-  int P = 1;
-  while (P < k) P <<= 1;
-  for (int e = k + threadIdx.x; e < P; e += kThreads) sh.sel[e] = INT32_MAX;
-  __syncthreads();
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int idx = threadIdx.x; idx < P; idx += kThreads) {
-        const int ixj = idx ^ j;
-        if (ixj > idx) {
-          const int32_t x = sh.sel[idx], y = sh.sel[ixj];
-          const bool asc = (idx & kk) == 0;
-          if ((x > y) == asc) {
-            sh.sel[idx] = y;
-            sh.sel[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (out)
-    for (int e = threadIdx.x; e < k; e += kThreads) out[e] = sh.sel[e];
-  if (a.sel_count && threadIdx.x == 0) a.sel_count[i] = k;
+  finish_query(a, sh, i, nc, out);
 }
 
 }  // namespace
