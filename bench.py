@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy 3 times (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -122,6 +124,16 @@ def main() -> int:
         return 2
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3}))
+        return 0
 
     from long_context_mqa_amd import hs2
     from workloads.configs import block_config, make_bridge_inputs, make_block_inputs
