@@ -48,15 +48,6 @@ __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c)
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane l's
-// bytes land at LDS address `lds` + 16*l. Issued as asm so that the wait for it can be
-// placed by hand (s_waitcnt vmcnt); it has no register outputs.
-__device__ inline void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n"
-               :
-               : "v"(g), "s"(lds)
-               : "memory", "m0");
-}
 
 template <int N>
 __device__ inline void wait_vmcnt() {

@@ -11,9 +11,10 @@
 // The 2L projection matrices are treated as one [d_model x 128*2L] right-hand side. The
 // weights are first transposed into the workspace (k contiguous), so that both MFMA
 // operands read 16 contiguous bytes per lane. Each workgroup computes a 256-row x
-// 256-column tile of C^T = W^T H^T (two output matrices) with four waves of 128 x 128;
-// tiles of the same rows run back to back on one XCD, so H is read from HBM once and
-// re-served from that XCD's L2 for the other column tiles.
+// 256-column tile of C^T = W^T H^T (two output matrices) with four waves of 128 x 128
+// (accumulators in the AGPRs); operand tiles stream through three LDS stages by
+// direct-to-LDS loads. Tiles of the same rows run back to back on one XCD, so H is read
+// from HBM once and re-served from that XCD's L2 for the other column tiles.
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -24,7 +25,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;   // H rows per workgroup
 constexpr int kBN = 256;   // output columns per workgroup (two matrices of 128)
-constexpr int kBK = 64;    // contraction step
 constexpr int kXcds = 8;
 
 struct WPtrs {
@@ -48,26 +48,62 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(WPtrs wp, uint16_t* wt
   }
 }
 
-__device__ inline int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+constexpr int kStagesG = 3;      // LDS stages of the contraction loop
+constexpr int kKStep = 32;       // contraction step (two MFMA k-steps of 16)
+constexpr int kTileB = 256 * kKStep * 2;  // 16 KB: one 256 x 32 bf16 operand tile
+
+// Operand tiles in LDS: 256 rows of 64 bytes (32 bf16 of the contraction); the 16-byte
+// chunk c of row r sits at chunk position c ^ ((r >> 2) & 3), so that the eight lanes an
+// LDS read serves together (eight consecutive rows, same chunk) hit distinct banks.
+__device__ inline uint32_t op_off(int row, int chunk) {
+  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
+}
+
+struct GemmSmem {
+  uint8_t a[kStagesG][kTileB];  // transposed weights: [n][k]
+  uint8_t b[kStagesG][kTileB];  // hidden states:      [row][k]
+};
 
 __global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeArgs a) {
-  __shared__ __align__(16) uint16_t As[kBN * kBK];  // Wt tile [n][k]
-  __shared__ __align__(16) uint16_t Bs[kBM * kBK];  // H tile  [row][k]
+  __shared__ __align__(16) GemmSmem sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_nt = a.n_mats / 2;
   const int64_t n_rt = (a.n_rows + kBM - 1) / kBM;
   // XCD-aware order: workgroup b runs on XCD b % 8; consecutive slots of one XCD take
-  // the column tiles of one row tile.
+  // the column tiles of one row tile, so the H rows are re-read from that XCD's L2.
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int64_t rt = (int64_t)(slot / n_nt) * kXcds + xcd;
   const int nt = slot % n_nt;
   if (rt >= n_rt) return;
   const int64_t r0 = rt * kBM;
-
   const uint16_t* wt = a.wt + (size_t)nt * kBN * a.d_model;
   const int wr = wave & 1;   // 128-row half
   const int wn = wave >> 1;  // 128-column half (one output matrix)
+
+  const uint32_t la0 = (uint32_t)(size_t)sm.a[0];
+  const uint32_t lb0 = (uint32_t)(size_t)sm.b[0];
+  // this wave's copy rows: copies r = 4*wave .. 4*wave+3 cover rows 16r .. 16r+15
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * wave + q;
+    const int row = 16 * r + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    ga[q] = wt + (size_t)row * a.d_model + chunk * 8;
+    int64_t hr = r0 + row;
+    if (hr >= a.n_rows) hr = a.n_rows - 1;
+    gb[q] = a.h + hr * a.d_model + chunk * 8;
+  }
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * wave + q;
+      dma16(ga[q] + kt * kKStep, __builtin_amdgcn_readfirstlane(la0 + st * kTileB + r * 1024));
+      dma16(gb[q] + kt * kKStep, __builtin_amdgcn_readfirstlane(lb0 + st * kTileB + r * 1024));
+    }
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -75,41 +111,26 @@ __global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
 
-  uint4 ra[8], rb[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = threadIdx.x + 256 * r;
-      const int row = e >> 3, c = e & 7;
-      ra[r] = *reinterpret_cast<const uint4*>(wt + (size_t)row * a.d_model + k0 + 8 * c);
-      int64_t hr = r0 + row;
-      if (hr >= a.n_rows) hr = a.n_rows - 1;
-      rb[r] = *reinterpret_cast<const uint4*>(a.h + hr * a.d_model + k0 + 8 * c);
-    }
-  };
-  const int KT = a.d_model / kBK;
-  gload(0);
+  const int KT = a.d_model / kKStep;
+  issue(0, 0);
+  if (KT > 1) issue(1, 1);
   for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
+    const int st = kt % kStagesG;
+    // this wave's 8 copies of stage kt have landed once only those of stage kt+1 remain
+    if (kt + 1 < KT)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // the whole stage has landed; stage kt-1 is no longer read
+    if (kt + 2 < KT) issue(kt + 2, (kt + 2) % kStagesG);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = threadIdx.x + 256 * r;
-      const int row = e >> 3, c = e & 7;
-      *reinterpret_cast<uint4*>(&As[swz(row, c)]) = ra[r];
-      *reinterpret_cast<uint4*>(&Bs[swz(row, c)]) = rb[r];
-    }
-    __syncthreads();
-    if (kt + 1 < KT) gload((kt + 1) * kBK);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       const int c = 2 * ks + (lane >> 5);
       bf16x8 av[4], bv[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int nrow = wn * 128 + 32 * x + (lane & 31);
-        av[x] = *reinterpret_cast<const bf16x8*>(&As[swz(nrow, c)]);
-        const int hrow = wr * 128 + 32 * x + (lane & 31);
-        bv[x] = *reinterpret_cast<const bf16x8*>(&Bs[swz(hrow, c)]);
+        av[x] = *reinterpret_cast<const bf16x8*>(sm.a[st] + op_off(wn * 128 + 32 * x + (lane & 31), c));
+        bv[x] = *reinterpret_cast<const bf16x8*>(sm.b[st] + op_off(wr * 128 + 32 * x + (lane & 31), c));
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x)

@@ -137,6 +137,24 @@ __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t
   return ok;
 }
 
+// One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane l's
+// 16 bytes land at LDS byte address `lds` + 16*l (`lds` must be wave-uniform). Issued as
+// asm so that the wait for it can be placed by hand with s_waitcnt vmcnt (the compiler
+// otherwise waits for every pending LDS copy before any LDS read). The asm has no
+// register results; M0, which holds the LDS address, is saved and restored around it.
+__device__ inline void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0\n"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
 // Number of logical keys of a query: t+1 (full causal) or top_k + min(window, t+1)
 // (gather: selected slots first, then the window rows oldest first).
 __device__ inline int logical_keys(bool gather, int t, int window, int top_k) {
