@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhs2.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "hs2_api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_chunk.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "hs2_api.cpp"]
 
 
 def hipcc() -> str:

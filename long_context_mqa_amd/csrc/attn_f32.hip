@@ -130,6 +130,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, uint32_t* his
     if (sl == 0) {
       P->m[h] = m;
       P->l[h] = l;
+      P->le[h] = l;
     }
 #pragma unroll
     for (int r = 0; r < 32; ++r) P->o[(32 * sl + r) * kHeads + h] = o[r];

@@ -34,7 +34,8 @@ hs2_status ok() {
 constexpr size_t kAlign = 256;
 constexpr int kTargetGroups = 256;  // workgroups per launch: one per CU
 constexpr int kMaxSplit = 256;      // bound of the split combine
-constexpr int kSparseSplitMax = 2048;  // keys per sparse workgroup (LDS row list)
+constexpr int kSparseSplitMax = 2048;
+constexpr int kChunkMinQueries = 8;   // queries per sequence from which K/V tiles are shared  // keys per sparse workgroup (LDS row list)
 constexpr int kFilterLen = 8192;    // candidates per top-k filter workgroup (256 threads x 32)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -70,6 +71,9 @@ int64_t launch_work(const hs2_seqs* b, int64_t max_keys) {
 }
 
 struct SelectPlan {
+  bool chunk = false;     // many queries per sequence: q-tile kernels sharing K/V tiles
+  int max_tiles = 0;      // q-tiles launched (upper bound of the tiles of the batch)
+  size_t off_tiles = 0;
   Split attn, score;
   int f_split = 1, f_len = kFilterLen;
   int64_t score_stride = 0;
@@ -77,23 +81,43 @@ struct SelectPlan {
          off_above = 0, off_cand = 0, total = 0;
 };
 
-SelectPlan plan_select(const hs2_seqs* b, int window, int top_k) {
+SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
   SelectPlan p;
   const int64_t tq = std::max(0, b->total_q);
-  p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
   const int64_t max_cand = std::max<int64_t>(0, (int64_t)b->max_kv_len - window + 1);
-  p.score = plan_split(launch_work(b, max_cand), max_cand);
+  p.chunk = dt == HS2_BF16 && b->max_q_per_seq >= kChunkMinQueries;
+  if (p.chunk) {
+    // q-tiles of kWaves queries of one sequence; splits fill one round of workgroups
+    p.max_tiles = (int)(tq / kWaves + b->num_seqs + 1);
+    const int64_t want = std::max<int64_t>(1, kTargetGroups / std::max(1, p.max_tiles));
+    auto split_of = [&](int64_t keys) {
+      Split sp;
+      if (keys <= 0) return Split{1, kTile};
+      sp.split_keys = (int)(ceil_div(ceil_div(keys, std::min<int64_t>(want, kMaxSplit)), kTile) * kTile);
+      sp.n_split = (int)ceil_div(keys, sp.split_keys);
+      return sp;
+    };
+    p.attn = split_of(b->max_kv_len);
+    p.score = split_of(max_cand);
+  } else {
+    p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
+    p.score = plan_split(launch_work(b, max_cand), max_cand);
+  }
   p.f_split = (int)std::max<int64_t>(1, ceil_div(max_cand, kFilterLen));
   p.score_stride = (max_cand + 63) / 64 * 64;
   size_t off = 0;
   p.off_part = off;
-  if (p.attn.n_split > 1) off += align_up((size_t)tq * p.attn.n_split * sizeof(Partial));
+  if (p.attn.n_split > 1 || p.chunk) off += align_up((size_t)tq * p.attn.n_split * sizeof(Partial));
   p.off_lse2 = off;
   off += align_up((size_t)tq * kHeads * sizeof(float));
   p.off_hist = off;
   off += align_up((size_t)tq * kHistBins * sizeof(uint32_t));
   p.off_counters = off;
   off += align_up((size_t)tq * 4 * sizeof(uint32_t));
+  if (p.chunk) {
+    p.off_tiles = off;
+    off += align_up((size_t)p.max_tiles * sizeof(int2));
+  }
   if (top_k > 0) {
     p.off_scores = off;
     off += align_up((size_t)tq * p.score_stride * sizeof(float));
@@ -225,9 +249,8 @@ size_t hs2_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_head
                                            int32_t window, int32_t top_k, hs2_dtype dt) {
   (void)n_heads;
   (void)head_dim;
-  (void)dt;
   if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
-  return plan_select(batch, window, top_k).total;
+  return plan_select(batch, window, top_k, dt).total;
 }
 
 hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
@@ -241,7 +264,7 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     return fail(HS2_ERR_INVALID_ARG, "sel_idx must not be NULL when top_k > 0");
   if ((sel_idx && !aligned(sel_idx, 4)) || (sel_count && !aligned(sel_count, 4)))
     return fail(HS2_ERR_INVALID_ARG, "sel_idx and sel_count must be 4-byte aligned");
-  const SelectPlan p = plan_select(batch, window, top_k);
+  const SelectPlan p = plan_select(batch, window, top_k, dt);
   if (workspace_bytes < p.total || (p.total > 0 && !workspace))
     return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
                 p.total);
@@ -271,13 +294,24 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
   a.lse = lse;
   a.lse2 = lse2;
   const int grid = tq * p.attn.n_split;
+  int2* tiles = p.chunk ? at<int2>(workspace, p.off_tiles) : nullptr;
   LaunchMarks mk(s);
-  hipError_t e = mk.before(0);
-  if (e == hipSuccess)
-    e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s) : launch_attn_bf16(a, false, grid, hist, counters, s);
+  hipError_t e = hipSuccess;
+  if (p.chunk) {
+    a.part = at<Partial>(workspace, p.off_part);
+    e = launch_qtile_prep(a.b, tiles, p.max_tiles, s);
+    if (e != hipSuccess) return hip_fail(e, "q-tile list launch");
+  }
+  e = mk.before(0);
+  if (e == hipSuccess) {
+    if (p.chunk)
+      e = launch_attn_chunk(a, tiles, p.max_tiles, s);
+    else
+      e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s) : launch_attn_bf16(a, false, grid, hist, counters, s);
+  }
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "full attention launch");
-  if (p.attn.n_split > 1) {
+  if (p.attn.n_split > 1 || p.chunk) {
     CombineArgs c{};
     c.b = a.b;
     c.part = a.part;
@@ -325,7 +359,12 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     sc.scores = at<float>(workspace, p.off_scores);
     sc.hist = hist;
     e = mk.before(2);
-    if (e == hipSuccess) e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+    if (e == hipSuccess) {
+      if (p.chunk)
+        e = launch_score_chunk(sc, tiles, p.max_tiles, s);
+      else
+        e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+    }
     if (e == hipSuccess) e = mk.after(2);
     if (e != hipSuccess) return hip_fail(e, "score launch");
     e = mk.before(3);

@@ -33,10 +33,13 @@ struct SeqsDev {
 };
 
 // Partial result of one workgroup's key range for one query: running max m (log2
-// domain), softmax denominator l, and the unnormalised output transposed to [dim][head].
+// domain), the softmax denominator summed from the probabilities as rounded for the
+// P.V product (l, normalises the output) and from the unrounded probabilities (le, gives
+// the LSE), and the unnormalised output transposed to [dim][head].
 struct Partial {
   float m[kHeads];
   float l[kHeads];
+  float le[kHeads];
   float o[kDim * kHeads];
 };
 
@@ -143,6 +146,7 @@ __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t
 // otherwise waits for every pending LDS copy before any LDS read). The asm has no
 // register results; M0, which holds the LDS address, is saved and restored around it.
 __device__ inline void dma16(const void* g, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -169,6 +173,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, bool gather, int grid, uint32_t* 
 hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
                            uint32_t* counters, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
+hipError_t launch_qtile_prep(const SeqsDev& b, int2* tiles, int max_tiles, hipStream_t s);
+hipError_t launch_attn_chunk(const AttnArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
+hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s);

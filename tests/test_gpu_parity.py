@@ -116,6 +116,20 @@ def test_ragged_small_contexts(dtype):
     check_all_queries_properties(inp, g)
 
 
+def test_chunked_ragged_queries():
+    """Many queries per sequence (the q-tile kernels): query counts not multiples of the
+    tile size, queries with t < window and with at most k candidates in the same tile."""
+    spec = BlockSpec("chunked", [3000, 9000, 700],
+                     [list(range(2980, 2993)), [8999, 8000, 7000, 5000, 4000, 1200, 1100, 127],
+                      [699, 698, 500, 400, 300, 200, 127, 5, 0]],
+                     dtype="bf16", n_sparse=1, needles_per_query=1, seed=19)
+    inp = make_block_inputs(spec)
+    _say("chunked ragged")
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), "chunked")
+    check_all_queries_properties(inp, g)
+
+
 def test_small_context_sparse_equals_full_on_gpu():
     """When t+1 <= window + top_k, the sparse layer with the selector's own Q reproduces
     the selector's output (the <= 1,152-row invariant)."""
