@@ -19,13 +19,13 @@
 // 0..7, so each lane loads one contiguous 128-byte half row of K and of Q.
 //
 // Pass 1 computes S^T = K Q^T (keys as rows, heads as columns), so each lane owns two
-// heads and sees 16 keys of a 32-key tile: the per-head running max is an in-register
-// reduction plus one exchange with lane l^32. The probabilities P^T in the C layout are
+// heads and sees 16 keys of a 32-key tile. The probabilities P^T in the C layout are
 // already the B operand of O^T = V^T P^T when the key index of each 16-key step is
-// permuted to match; V^T comes from a per-wave LDS copy of the V tile.
-// Softmax runs in the log2 domain (x = scale*log2(e)*s) with a lazily moved reference:
-// the running max only moves when a tile exceeds it by more than 8, which keeps every
-// exponent <= 2^8 while avoiding a rescale of the 128 accumulators on most tiles.
+// permuted to match; the V^T operands come from transposing LDS reads of the V tile.
+// Softmax runs in the log2 domain (x = scale*log2(e)*s). The reference of each head is
+// fixed at the wave's first tile with an attended key, so the accumulators are never
+// rescaled inside the key loop; a wave whose sums overflowed (a logit more than ~100
+// above that first maximum) recomputes its keys with its exact maximum as reference.
 // P is rounded to bf16 for the MFMA and the output's denominator sums the same rounded
 // values, so the output is an exactly normalised average of V rows; the LSE uses the sum
 // of the unrounded values.
@@ -40,6 +40,7 @@ using namespace attn;
 // then the cross-wave merge; Q (in MFMA operand order) and the gathered row list stay
 // outside the union.
 constexpr int kSelMax = 2048;  // gathered slots per workgroup (the host caps the split)
+constexpr int kSelPerThread = kSelMax / 256;
 
 struct AttnSmem {
   union {
@@ -51,21 +52,95 @@ struct AttnSmem {
       float fm[kHeads];
       float fl[kHeads];
       float fle[kHeads];
-      float o[kDim][kHeads + 1];
+      // per-wave O^T scaled to the common reference: [wave][d][h ^ 32 * ((d >> 2) & 1)]
+      float o[kWaves][kDim * kHeads];
     } mg;
   };
   uint8_t q[kHeads * kDim * 2];
   int32_t sel[kSelMax];
 };
 
+// Streams the tiles wave, wave + 4, ... of the workgroup's key range through the wave's
+// two LDS stages. DMA groups are issued in the order K0 V0 K1 V1, then per iteration
+// K(it+2) right after the K operands of tile it are in registers and V(it+2) after its
+// PV step, so two tiles stream in while one is computed. Waits count the 8-load groups
+// issued later. kMaxOnly: only the logit maximum of the attended keys (into mx).
+template <bool kMaxOnly>
+__device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem& sm, const KeyList& kl, int k0, int k1,
+                                    int ntiles, const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
+                                    float c2, int wave, int lane) {
+  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  uint32_t lk[kStages], lv[kStages];
+#pragma unroll
+  for (int sidx = 0; sidx < kStages; ++sidx) {
+    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][0]);
+    lv[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][1]);
+  }
+  uint32_t vb[4];
+  vt_bases(lane, vb);
+  uint32_t okm[kStages] = {0u, 0u};
+  int relv[kStages] = {0, 0};
+  for (int it = 0; it < min(ntw, kStages); ++it) {
+    okm[it] = tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, relv[it]);
+    issue_rows<true>(kp, kl.base, relv[it], lane, lk[it]);
+    issue_rows<false>(vp, kl.base, relv[it], lane, lv[it]);
+  }
+  for (int it = 0; it < ntw; ++it) {
+    const int sidx = it & 1;
+    const bool more1 = it + 1 < ntw, more2 = it + 2 < ntw;
+    wait_vmcnt_dyn(more1 ? 24 : 8);  // K(it) has landed
+    bf16x8 kop[8];
+    read_k(sm.stage[wave][sidx][0], lane, kop);
+    const uint32_t vm = okm[sidx];
+    int rel2 = 0;
+    if (more2) {
+      okm[sidx] = tile_rows(kl, k0 + (wave + (it + 2) * kWaves) * kTile, k1, lane, rel2);
+      issue_rows<true>(kp, kl.base, rel2, lane, lk[sidx]);
+    }
+    wait_vmcnt_dyn((more1 ? 16 : 0) + (more2 ? 8 : 0));  // V(it) has landed
+    if (vm != 0u) {
+      if (kMaxOnly)
+        process_tile_max<false>(mx, sm.q, nullptr, kop, vm, c2, lane);
+      else
+        process_tile<false>(st, sm.q, nullptr, kop, sm.stage[wave][sidx][1], vb, vm, c2, lane);
+    }
+    if (more2) issue_rows<false>(vp, kl.base, rel2, lane, lv[sidx]);
+  }
+}
+
 template <bool kGather>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hist,
                                                         uint32_t* counters) {
   __shared__ __align__(16) AttnSmem sm;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x / a.n_split;
   const int split = blockIdx.x - i * a.n_split;
+  const int k0 = split * a.split_keys;
+
+  // Loads that do not depend on the query's position go out first: the gathered slots
+  // of this split (gather mode: the key count exceeds top_k, so the slot range is known)
+  // and Q in MFMA operand order: 16-byte piece (nb, s, lane) = Q[32nb + l%32][(l/32)*64 + 8s ..]
+  int32_t selv[kSelPerThread];
+  const int s1 = kGather ? min(min(a.top_k, k0 + a.split_keys), k0 + kSelMax) : 0;
+  if (kGather) {
+    const int32_t* selr = a.sel + (size_t)i * a.top_k;
+#pragma unroll
+    for (int u = 0; u < kSelPerThread; ++u) {
+      const int p = k0 + (int)threadIdx.x + 256 * u;
+      selv[u] = p < s1 ? selr[p] : -1;
+    }
+  }
+  bf16x8 qv[4];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)i * kHeads * kDim;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = (int)threadIdx.x + 256 * u;
+      const int ln = e & 63, sidx = (e >> 6) & 7, nb = e >> 9;
+      qv[u] = *reinterpret_cast<const bf16x8*>(qp + (32 * nb + (ln & 31)) * kDim + (ln >> 5) * 64 + sidx * 8);
+    }
+  }
 
   int64_t base;
   int t;
@@ -94,74 +169,37 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
   kl.n_keys = logical_keys(kGather, t, a.window, a.top_k);
   kl.w_eff = min(a.window, t + 1);
   kl.cand_hi = t - a.window;
-  const int k0 = split * a.split_keys;
   if (k0 >= kl.n_keys) return;  // empty split: the combine does not read it
   const int k1 = min(kl.n_keys, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
   kl.sel_lds = sm.sel;
   kl.sel_k0 = k0;
   if (kGather) {
-    const int32_t* selr = a.sel + (size_t)i * a.top_k;
-    const int s1 = min(min(k1, a.top_k), k0 + kSelMax);
-    for (int p = k0 + threadIdx.x; p < s1; p += blockDim.x) sm.sel[p - k0] = selr[p];
-  }
-  // Q^T B-operands in LDS: 16-byte piece (nb, s, lane) = Q[32*nb + l%32][(l/32)*64 + 8*s ..]
-  {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)i * kHeads * kDim;
-    for (int e = threadIdx.x; e < 16 * 64; e += blockDim.x) {
-      const int ln = e & 63, sidx = (e >> 6) & 7, nb = e >> 9;
-      *reinterpret_cast<uint4*>(sm.q + e * 16) = *reinterpret_cast<const uint4*>(
-          qp + (32 * nb + (ln & 31)) * kDim + (ln >> 5) * 64 + sidx * 8);
+#pragma unroll
+    for (int u = 0; u < kSelPerThread; ++u) {
+      const int p = k0 + (int)threadIdx.x + 256 * u;
+      if (p < s1) sm.sel[p - k0] = selv[u];
     }
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8*>(sm.q + ((int)threadIdx.x + 256 * u) * 16) = qv[u];
   __syncthreads();
 
   const __bf16* kp = static_cast<const __bf16*>(a.k);
   const __bf16* vp = static_cast<const __bf16*>(a.v);
-
   WaveState st;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    st.m[nb] = kNegBig;
-    st.l[nb] = 0.0f;
-    st.le[nb] = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) st.o[nb][mb] = f32x16{};
-  }
-
-  // Tiles of this wave: wave, wave + 4, ...  Two LDS stages each for K and V. DMA groups
-  // are issued in the order K0 V0 K1 V1, then per iteration K(it+2) right after the K
-  // operands of tile it are in registers and V(it+2) after its PV step, so two tiles
-  // stream in while one is computed. Waits count the 8-load groups issued later.
-  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  uint32_t lk[kStages], lv[kStages];
-#pragma unroll
-  for (int sidx = 0; sidx < kStages; ++sidx) {
-    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][0]);
-    lv[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][1]);
-  }
-  uint32_t okm[kStages] = {0u, 0u};
-  int relv[kStages] = {0, 0};
-  for (int it = 0; it < min(ntw, kStages); ++it) {
-    okm[it] = tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, relv[it]);
-    issue_rows<true>(kp, base, relv[it], lane, lk[it]);
-    issue_rows<false>(vp, base, relv[it], lane, lv[it]);
-  }
-  for (int it = 0; it < ntw; ++it) {
-    const int sidx = it & 1;
-    const bool more1 = it + 1 < ntw, more2 = it + 2 < ntw;
-    wait_vmcnt_dyn(more1 ? 24 : 8);            // K(it) has landed
-    bf16x8 kop[8];
-    read_k(sm.stage[wave][sidx][0], lane, kop);
-    const uint32_t vm = okm[sidx];
-    int rel2 = 0;
-    if (more2) {
-      okm[sidx] = tile_rows(kl, k0 + (wave + (it + 2) * kWaves) * kTile, k1, lane, rel2);
-      issue_rows<true>(kp, base, rel2, lane, lk[sidx]);
-    }
-    wait_vmcnt_dyn((more1 ? 16 : 0) + (more2 ? 8 : 0));   // V(it) has landed
-    process_tile<false>(st, sm.q, nullptr, kop, sm.stage[wave][sidx][1], vm, a.c2, lane);
-    if (more2) issue_rows<false>(vp, base, rel2, lane, lv[sidx]);
+  state_init(st);
+  float mx[2] = {-INFINITY, -INFINITY};
+  stream_tiles<false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+  if (!state_finite(st)) {
+    // rare: a logit far above the first tile's maximum overflowed the sums; recompute
+    // with the exact maximum of this wave's keys as reference (every weight <= 1)
+    stream_tiles<true>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+    state_init(st);
+    st.m[0] = mx[0];
+    st.m[1] = mx[1];
+    st.have_ref = 1;
+    stream_tiles<false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
   }
 
 #pragma unroll
@@ -181,57 +219,65 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
     }
   }
   __syncthreads();
-  float alpha[2];
+  {
+    float alpha[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int h = 32 * nb + (lane & 31);
-    float M = sm.mg.m[0][h];
+    for (int nb = 0; nb < 2; ++nb) {
+      const int h = 32 * nb + (lane & 31);
+      float M = sm.mg.m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][h]);
-    alpha[nb] = fast_exp2(st.m[nb] - M);
-  }
-  if (threadIdx.x < kHeads) {
-    const int h = threadIdx.x;
-    float M = sm.mg.m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][h]);
-    float L = 0.0f, LE = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(sm.mg.m[w][h] - M);
-      L += sm.mg.l[w][h] * f;
-      LE += sm.mg.le[w][h] * f;
-    }
-    sm.mg.fm[h] = M;
-    sm.mg.fl[h] = L;
-    sm.mg.fle[h] = LE;
-  }
-  const int hrow = 4 * (lane >> 5);
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int d = 32 * mb + 8 * (j >> 2) + hrow + (j & 3);
-            const int h = 32 * nb + (lane & 31);
-            const float val = st.o[nb][mb][j] * alpha[nb];
-            sm.mg.o[d][h] = (w == 0) ? val : sm.mg.o[d][h] + val;
-          }
-    }
-    __syncthreads();
-  }
-
-  if (a.n_split == 1) {
-    __bf16* out = static_cast<__bf16*>(a.out) + (size_t)i * kHeads * kDim;
-    for (int e = threadIdx.x; e < kHeads * kDim; e += blockDim.x) {
-      const int h = e >> 7, d = e & 127;
-      out[e] = (__bf16)(sm.mg.o[d][h] / sm.mg.fl[h]);
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][h]);
+      alpha[nb] = fast_exp2(st.m[nb] - M);
     }
     if (threadIdx.x < kHeads) {
       const int h = threadIdx.x;
+      float M = sm.mg.m[0][h];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][h]);
+      float L = 0.0f, LE = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(sm.mg.m[w][h] - M);
+        L += sm.mg.l[w][h] * f;
+        LE += sm.mg.le[w][h] * f;
+      }
+      sm.mg.fm[h] = M;
+      sm.mg.fl[h] = L;
+      sm.mg.fle[h] = LE;
+    }
+    const int hrow = 4 * (lane >> 5);
+    float* ow = sm.mg.o[wave];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int d = 32 * mb + 8 * (j >> 2) + hrow + (j & 3);
+          const int h = 32 * nb + (lane & 31);
+          ow[d * kHeads + (h ^ (32 * ((d >> 2) & 1)))] = st.o[nb][mb][j] * alpha[nb];
+        }
+  }
+  __syncthreads();
+
+  // thread (h, dq): dims 32dq .. 32dq+31 of head h, summed over the waves in order
+  const int h = threadIdx.x & 63, dq = threadIdx.x >> 6;
+  if (a.n_split == 1) {
+    __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)i * kHeads + h) * kDim + 32 * dq;
+    const float inv = 1.0f / sm.mg.fl[h];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 v;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int d = 32 * dq + 8 * c + r;
+        const int pos = d * kHeads + (h ^ (32 * ((d >> 2) & 1)));
+        const float sum = ((sm.mg.o[0][pos] + sm.mg.o[1][pos]) + sm.mg.o[2][pos]) + sm.mg.o[3][pos];
+        v[r] = (__bf16)(sum * inv);
+      }
+      *reinterpret_cast<bf16x8*>(out + 8 * c) = v;
+    }
+    if (threadIdx.x < kHeads) {
       const float l2 = sm.mg.fm[h] + __log2f(sm.mg.fle[h]);
       if (a.lse) a.lse[(size_t)i * kHeads + h] = l2 * kLn2;
       if (a.lse2) a.lse2[(size_t)i * kHeads + h] = l2;
@@ -239,13 +285,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hi
   } else {
     Partial* P = a.part + (size_t)i * a.n_split + split;
     if (threadIdx.x < kHeads) {
-      P->m[threadIdx.x] = sm.mg.fm[threadIdx.x];
-      P->l[threadIdx.x] = sm.mg.fl[threadIdx.x];
-      P->le[threadIdx.x] = sm.mg.fle[threadIdx.x];
+      P->m[h] = sm.mg.fm[h];
+      P->l[h] = sm.mg.fl[h];
+      P->le[h] = sm.mg.fle[h];
     }
-    for (int e = threadIdx.x; e < kHeads * kDim; e += blockDim.x) {
-      const int d = e >> 6, h = e & 63;
-      P->o[e] = sm.mg.o[d][h];
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) {
+      const int d = 32 * dq + r;
+      const int pos = d * kHeads + (h ^ (32 * ((d >> 2) & 1)));
+      P->o[d * kHeads + h] = ((sm.mg.o[0][pos] + sm.mg.o[1][pos]) + sm.mg.o[2][pos]) + sm.mg.o[3][pos];
     }
   }
 }
@@ -362,7 +410,7 @@ struct ScoreSmem {
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
   __shared__ __align__(16) ScoreSmem sm;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = blockIdx.x / a.n_split;
   const int split = blockIdx.x - i * a.n_split;
   int64_t base;

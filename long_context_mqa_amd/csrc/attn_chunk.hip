@@ -87,6 +87,7 @@ struct ChunkSmem {
   };
   int tq[kQT];
   int64_t base[kQT];
+  int redo[kQT];
 };
 
 // Per-wave query of a q-tile; returns false if the wave has no valid query.
@@ -107,14 +108,52 @@ __device__ inline void issue_shared(const __bf16* __restrict__ kp, const __bf16*
     const int p = min(p0 + row, plast);
     const int64_t g = (base + p) * kDim;
     dma16(kp + g + ((lane & 15) ^ (row & 15)) * 8, lk + r * 1024);
-    dma16(vp + g + (lane & 15) * 8, lv + r * 1024);
+    dma16(vp + g + v_chunk(row, lane & 15) * 8, lv + r * 1024);
+  }
+}
+
+// Streams the tiles of [k0, k1) through the shared stages; every wave issues its share
+// of each tile's copies and takes part in every barrier. Waves with `compute` set run the
+// tile step on the keys their query attends (kMaxOnly: only the logit maximum, into mx).
+template <bool kMaxOnly>
+__device__ inline void chunk_stream(WaveState& st, float (&mx)[2], ChunkSmem& sm, const bf16x8 (&qop)[2][8],
+                                    bool compute, int t, int k0, int k1, int ntiles, int64_t seq_base,
+                                    const __bf16* __restrict__ kp, const __bf16* __restrict__ vp, float c2,
+                                    int wave, int lane) {
+  const uint32_t l0 = (uint32_t)(size_t)sm.stage[0][0];
+  auto lk = [&](int sidx) { return __builtin_amdgcn_readfirstlane(l0 + sidx * 2 * kTileBytes); };
+  auto lv = [&](int sidx) { return __builtin_amdgcn_readfirstlane(l0 + sidx * 2 * kTileBytes + kTileBytes); };
+  uint32_t vb[4];
+  vt_bases(lane, vb);
+
+  for (int it = 0; it < min(ntiles, kCStages - 1); ++it)
+    issue_shared(kp, vp, seq_base, k0 + it * kTile, k1 - 1, wave, lane, lk(it), lv(it));
+  for (int it = 0; it < ntiles; ++it) {
+    const int sidx = it % kCStages;
+    if (it + 1 < ntiles) wait_vmcnt<2 * kCopiesPerWave>(); else wait_vmcnt<0>();
+    loop_barrier();  // every wave's copies of tile it have landed; tile it-1 is released
+    if (it + kCStages - 1 < ntiles) {
+      const int nx = it + kCStages - 1;
+      issue_shared(kp, vp, seq_base, k0 + nx * kTile, k1 - 1, wave, lane, lk(nx % kCStages), lv(nx % kCStages));
+    }
+    const int p0 = k0 + it * kTile;
+    if (compute && p0 <= t) {
+      bf16x8 kop[8];
+      read_k(sm.stage[sidx][0], lane, kop);
+      const int nvalid = min(t, k1 - 1) - p0 + 1;  // keys p0 .. p0+nvalid-1 are attended
+      const uint32_t vm = __builtin_amdgcn_readfirstlane(nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u));
+      if (kMaxOnly)
+        process_tile_max<true>(mx, nullptr, qop, kop, vm, c2, lane);
+      else
+        process_tile<true>(st, nullptr, qop, kop, sm.stage[sidx][1], vb, vm, c2, lane);
+    }
   }
 }
 
 __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2* __restrict__ qtiles) {
   __shared__ __align__(16) ChunkSmem sm;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tix = blockIdx.x / a.n_split;
   const int split = blockIdx.x - tix * a.n_split;
   const int2 td = qtiles[tix];
@@ -161,38 +200,28 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
   }
 
   WaveState st;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    st.m[nb] = kNegBig;
-    st.l[nb] = 0.0f;
-    st.le[nb] = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) st.o[nb][mb] = f32x16{};
-  }
+  state_init(st);
+  float mx[2] = {-INFINITY, -INFINITY};
   const __bf16* kp = static_cast<const __bf16*>(a.k);
   const __bf16* vp = static_cast<const __bf16*>(a.v);
-  const uint32_t l0 = (uint32_t)(size_t)sm.stage[0][0];
-  auto lk = [&](int sidx) { return __builtin_amdgcn_readfirstlane(l0 + sidx * 2 * kTileBytes); };
-  auto lv = [&](int sidx) { return __builtin_amdgcn_readfirstlane(l0 + sidx * 2 * kTileBytes + kTileBytes); };
+  const int tu = __builtin_amdgcn_readfirstlane(t);  // one query per wave
+  chunk_stream<false>(st, mx, sm, qop, mine, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
 
-  for (int it = 0; it < min(ntiles, kCStages - 1); ++it)
-    issue_shared(kp, vp, seq_base, k0 + it * kTile, k1 - 1, wave, lane, lk(it), lv(it));
-  for (int it = 0; it < ntiles; ++it) {
-    const int sidx = it % kCStages;
-    if (it + 1 < ntiles) wait_vmcnt<2 * kCopiesPerWave>(); else wait_vmcnt<0>();
-    loop_barrier();  // every wave's copies of tile it have landed; tile it-1 is released
-    if (it + kCStages - 1 < ntiles) {
-      const int nx = it + kCStages - 1;
-      issue_shared(kp, vp, seq_base, k0 + nx * kTile, k1 - 1, wave, lane, lk(nx % kCStages), lv(nx % kCStages));
+  // rare: a wave whose sums overflowed recomputes with its exact logit maximum; the
+  // workgroup streams the tiles again together
+  const bool bad = mine && !state_finite(st);
+  if (lane == 0) sm.redo[wave] = bad ? 1 : 0;
+  __syncthreads();
+  if (sm.redo[0] | sm.redo[1] | sm.redo[2] | sm.redo[3]) {
+    chunk_stream<true>(st, mx, sm, qop, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
+    if (bad) {
+      state_init(st);
+      st.m[0] = mx[0];
+      st.m[1] = mx[1];
+      st.have_ref = 1;
     }
-    const int p0 = k0 + it * kTile;
-    if (mine && p0 <= t) {
-      bf16x8 kop[8];
-      read_k(sm.stage[sidx][0], lane, kop);
-      const int nvalid = min(t, k1 - 1) - p0 + 1;  // keys p0 .. p0+nvalid-1 are attended
-      const uint32_t vm = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-      process_tile<true>(st, nullptr, qop, kop, sm.stage[sidx][1], vm, a.c2, lane);
-    }
+    __syncthreads();
+    chunk_stream<false>(st, mx, sm, qop, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
   }
 
   if (!mine) return;
@@ -244,7 +273,7 @@ struct ScoreChunkSmem {
 __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int2* __restrict__ qtiles) {
   __shared__ __align__(16) ScoreChunkSmem sm;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tix = blockIdx.x / a.n_split;
   const int split = blockIdx.x - tix * a.n_split;
   const int2 td = qtiles[tix];

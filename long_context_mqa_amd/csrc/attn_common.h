@@ -12,7 +12,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kNegBig = -1.0e30f; // "no key yet" reference
-constexpr float kLazy = 8.0f;       // reference moves only when exceeded by more than this
 constexpr int kTileBytes = kTile * kDim * 2;  // 8 KB: one K or V tile
 constexpr int kStages = 2;                    // per-wave LDS stages (K + V each)
 constexpr int kDmaPerHalf = kTileBytes / 1024;     // 8 wave-wide 16-byte loads per K or V tile
@@ -34,11 +33,12 @@ __device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : 
 // Tile layouts in LDS (32 rows of 256 bytes, filled by row-coalesced DMA):
 //  K: the 16-byte chunk c of row r is stored at chunk position c ^ (r & 15), so that the
 //     MFMA-operand reads (32 rows, same chunk) are free of bank conflicts;
-//  V: plain row-major, so that all V^T operand reads of a lane share one base address
-//     and differ by immediate offsets.
+//  V: chunk c of row r at position c ^ (4 * (r & 3)), so that the transposing reads of
+//     the V^T operands (8 rows x 64 bytes per instruction) cover all 64 banks twice.
 __device__ inline uint32_t tile_off(int row, int chunk) {
   return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4));
 }
+__device__ inline int v_chunk(int row, int pos) { return pos ^ ((row & 3) << 2); }
 
 // Logical key list of one query. Full mode: positions 0..t. Gather mode: top_k selected
 // slots (entries outside the candidate range are masked) followed by the window rows.
@@ -77,34 +77,89 @@ __device__ inline uint32_t tile_rows(const KeyList& kl, int p0, int p1, int lane
   return (uint32_t)__ballot(ok);
 }
 
-// Enqueues the 32 rows of a K tile (swizzled) or a V tile (row-major) into LDS. `rel` is
+// Enqueues the 32 rows of a K tile or a V tile (each in its swizzle) into LDS. `rel` is
 // the row of key l%32 held by lane l; earlier LDS reads of the stage must have completed.
-template <bool kSwizzle>
+// Copy r writes rows 4r .. 4r+3: lane l fills chunk position l%16 of row 4r + l/16.
+template <bool kIsK>
 __device__ inline void issue_rows(const __bf16* __restrict__ src, int64_t base, int rel, int lane, uint32_t lds) {
   wait_lgkm0();
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int row = r * 4 + (lane >> 4);
-    const int chunk = kSwizzle ? ((lane & 15) ^ (row & 15)) : (lane & 15);
+    const int chunk = kIsK ? ((lane & 15) ^ (row & 15)) : v_chunk(row, lane & 15);
     dma16(src + (base + __shfl(rel, row)) * kDim + chunk * 8, lds + r * 1024);
   }
 }
 
 // Online-softmax state of one wave: 64 heads x 128 dims, O^T in the C layout.
+// The softmax reference m of a head is fixed at the first tile that holds an attended
+// key (that tile's maximum); later tiles are not rescaled. exp2(x - m) may then exceed 1,
+// which floating point represents exactly up to 2^127; a wave whose state overflowed is
+// recomputed with the exact maximum as reference (see state_finite).
 struct WaveState {
   f32x16 o[2][4];   // [head block nb][dim block mb]
   float m[2];       // reference (log2 domain) of heads 32*nb + l%32
   float l[2];       // this lane's share of the denominator of the bf16-rounded P
   float le[2];      // ... and of the unrounded P (for the LSE)
+  int have_ref;     // wave-uniform: m holds a reference
 };
 
-// One 32-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T. Q^T operands and the V
-// tile are read from LDS; the K operands were read already (its stage is reused).
+__device__ inline void state_init(WaveState& st) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    st.m[nb] = kNegBig;
+    st.l[nb] = 0.0f;
+    st.le[nb] = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) st.o[nb][mb] = f32x16{};
+  }
+  st.have_ref = 0;
+}
+
+// True on every lane if no accumulator or denominator of the wave is inf or NaN.
+__device__ inline bool state_finite(const WaveState& st) {
+  float z = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    z = fmaf(st.l[nb], 0.0f, z);
+    z = fmaf(st.le[nb], 0.0f, z);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) z = fmaf(st.o[nb][mb][j], 0.0f, z);
+  }
+  return __all(z == 0.0f);  // inf * 0 and NaN * 0 are NaN
+}
+
+// Per-lane base addresses of the transposing V^T reads. Instruction (mb, ks, half) on
+// lane l returns V[16ks + 8half + 4(l/32) + i][32mb + l%32], i = 0..3: the A-operand
+// entries of MFMA k = 8(l/32) + 4half + i under the key order of the P^T operand.
+// Source lane l addresses row 16ks + 8half + 4(l/32) + (l/4)%4 at dims
+// 32mb + 16((l/16)%2) + 4(l%4) .. +3 (8 bytes).
+__device__ inline void vt_bases(int lane, uint32_t (&vb)[4]) {
+  const int r4 = lane & 3, c = (lane >> 2) & 3, gp = (lane >> 4) & 1, h = lane >> 5;
+  const uint32_t lb = (uint32_t)((4 * h + c) * 256 + 32 * gp + 8 * r4);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) vb[mb] = lb + 64u * (uint32_t)(mb ^ c);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ inline bf16x8 read_vt(const uint8_t* vt, uint32_t vbase, int ks) {
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(vt) + vbase + ks * 16 * 256;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 256));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S^T = K Q^T of one tile: acc[nb] holds keys (C rows) x heads 32nb.. (C columns).
 template <bool kQReg>
-__device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ qs, const bf16x8 (*qreg)[8],
-                                    const bf16x8 (&kop)[8], const uint8_t* __restrict__ vt, uint32_t vm, float c2,
-                                    int lane) {
-  f32x16 acc[2];
+__device__ inline void tile_logits(f32x16 (&acc)[2], const uint8_t* __restrict__ qs, const bf16x8 (*qreg)[8],
+                                   const bf16x8 (&kop)[8], int lane) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     acc[nb] = f32x16{};
@@ -114,82 +169,100 @@ __device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ q
       acc[nb] = mfma(kop[s], q, acc[nb]);
     }
   }
+}
 
+// Maximum over the attended keys of the tile (mask vm, bit = key) of the raw logits of
+// heads 32nb + l%32, times c2 (> 0); -inf if no key is attended.
+__device__ inline void tile_max(const f32x16 (&acc)[2], uint32_t vm, float c2, int lane, float (&mx)[2]) {
   const int hrow = 4 * (lane >> 5);
-  float x[2][16];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
+    float v = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[nb][j] = acc[nb][j] * c2;
-  if (vm != 0xffffffffu) {
+    for (int j = 0; j < 16; ++j) {
+      const int key = 8 * (j >> 2) + hrow + (j & 3);
+      v = ((vm >> key) & 1u) ? fmaxf(v, acc[nb][j]) : v;
+    }
+    v = fmaxf(v, __shfl_xor(v, 32));
+    mx[nb] = v * c2;
+  }
+}
+
+// One 32-key tile with at least one attended key: S^T = K Q^T, P = exp2(c2 S - m) with
+// the fixed reference, O^T += V^T P^T. Q^T operands come from LDS or registers, K
+// operands were read already, V^T is read from the tile's stage in LDS.
+template <bool kQReg>
+__device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ qs, const bf16x8 (*qreg)[8],
+                                    const bf16x8 (&kop)[8], const uint8_t* __restrict__ vt, const uint32_t (&vb)[4],
+                                    uint32_t vm, float c2, int lane) {
+  f32x16 acc[2];
+  tile_logits<kQReg>(acc, qs, qreg, kop, lane);
+  if (__builtin_amdgcn_readfirstlane(st.have_ref) == 0) {  // wave-uniform, first attended tile only
+    tile_max(acc, vm, c2, lane, st.m);
+    st.have_ref = 1;
+  }
+
+  float p[2][16];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float nm = -st.m[nb];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[nb][j] = fast_exp2(fmaf(acc[nb][j], c2, nm));
+  }
+  if (__builtin_amdgcn_readfirstlane(vm) != 0xffffffffu) {  // wave-uniform: edge tiles only
+    const int hrow = 4 * (lane >> 5);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = 8 * (j >> 2) + hrow + (j & 3);
-        if (!((vm >> key) & 1u)) x[nb][j] = -INFINITY;
+        if (!((vm >> key) & 1u)) p[nb][j] = 0.0f;
       }
-  }
-
-  float mx[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float v = x[nb][0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) v = fmaxf(v, x[nb][j]);
-    mx[nb] = fmaxf(v, __shfl_xor(v, 32));
-  }
-  const bool need0 = mx[0] > st.m[0] + kLazy;
-  const bool need1 = mx[1] > st.m[1] + kLazy;
-  if (__any(need0 || need1)) {
-    float alpha[2];
-    alpha[0] = need0 ? fast_exp2(st.m[0] - mx[0]) : 1.0f;
-    alpha[1] = need1 ? fast_exp2(st.m[1] - mx[1]) : 1.0f;
-    if (need0) st.m[0] = mx[0];
-    if (need1) st.m[1] = mx[1];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      st.l[nb] *= alpha[nb];
-      st.le[nb] *= alpha[nb];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st.o[nb][mb][j] *= alpha[nb];
-    }
   }
 
   // P^T (bf16) in the B-operand layout of the 16-key steps: step ks holds registers
   // j = 8*ks .. 8*ks+7, i.e. keys 16*ks + 8*(i/4) + 4*(l/32) + i%4.
   bf16x8 pb[2][2];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float lsum = 0.0f, esum = 0.0f;
+    float esum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pf = fast_exp2(x[nb][j] - st.m[nb]);
-      const __bf16 pv = (__bf16)pf;
-      pb[nb][j >> 3][j & 7] = pv;
-      lsum += (float)pv;
-      esum += pf;
+      pb[nb][j >> 3][j & 7] = (__bf16)p[nb][j];
+      esum += p[nb][j];
     }
-    st.l[nb] += lsum;
+    float lsum = st.l[nb];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[nb][ks][2 * u], pb[nb][ks][2 * u + 1]}, ones, lsum, false);
+    st.l[nb] = lsum;
     st.le[nb] += esum;
   }
 
-  // O^T += V^T P^T. A operand: lane l holds V[key][32*mb + l%32] for the 8 keys
-  // 16*ks + 8*(i/4) + 4*(l/32) + i%4 of its slots (row-major V tile: immediate offsets).
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(vt) + hrow * kDim + (lane & 31);
+  // O^T += V^T P^T
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 va;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii)
-        va[ii] = __builtin_bit_cast(__bf16, vb[(16 * ks + 8 * (ii >> 2) + (ii & 3)) * kDim + 32 * mb]);
+      const bf16x8 va = read_vt(vt, vb[mb], ks);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) st.o[nb][mb] = mfma(va, pb[nb][ks], st.o[nb][mb]);
     }
+}
+
+// Logit maximum only (the recomputation of an overflowed wave): mx = max(mx, tile max).
+template <bool kQReg>
+__device__ inline void process_tile_max(float (&mx)[2], const uint8_t* __restrict__ qs, const bf16x8 (*qreg)[8],
+                                        const bf16x8 (&kop)[8], uint32_t vm, float c2, int lane) {
+  f32x16 acc[2];
+  tile_logits<kQReg>(acc, qs, qreg, kop, lane);
+  float t[2];
+  tile_max(acc, vm, c2, lane, t);
+  mx[0] = fmaxf(mx[0], t[0]);
+  mx[1] = fmaxf(mx[1], t[1]);
 }
 
 // K A-operands of the 8 contraction steps from a swizzled K tile.

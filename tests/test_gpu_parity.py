@@ -297,3 +297,35 @@ def test_workload5_bridge_and_ragged_decode():
     del h, gk, gv
     torch.cuda.empty_cache()
     _full(5, [0, 13, 31])
+
+
+@pytest.mark.parametrize("shape", ["decode", "chunk"])
+def test_logit_far_above_first_tile_is_recomputed(shape):
+    """Keys whose logits for one head lie 150..402 (log2 units) above the other keys, at
+    increasing positions over ~16 tiles: a wave whose first tile holds none of them (or
+    a smaller one) overflows sums taken against that tile's maximum, and must detect it
+    and recompute with its exact maximum. Covers the decode-shaped selector kernel, the
+    q-tile selector kernel and the sparse kernel (whose Q equals the selector's, with
+    enough queries that its waves take two tiles each)."""
+    if shape == "decode":
+        spec = BlockSpec("spike-decode", [2000] * 40, [[1999]] * 40, dtype="bf16", n_sparse=1,
+                         needles_per_query=0, seed=21)
+    else:
+        spec = BlockSpec("spike-chunk", [5000], [list(range(4990, 5000))], dtype="bf16", n_sparse=1,
+                         needles_per_query=0, seed=22)
+    inp = make_block_inputs(spec)
+    qi, h = 0, 5
+    base = int(inp.kv_start[int(inp.q_seq[qi])])
+    qh = stored_to_f64(inp.q_sel[qi][h])
+    unit = qh / np.linalg.norm(qh)
+    c = spec.scale * math.log2(math.e) * np.linalg.norm(qh)  # x = c * alpha for k = alpha * unit
+    pos = 1000 + 8 * np.arange(64)
+    for j, pj in enumerate(pos):
+        inp.k[base + pj] = bf16_round(((150.0 + 4.0 * j) / c * unit).astype(np.float32))
+    inp.q_sp[0][qi] = inp.q_sel[qi]
+    xs = spec.scale * math.log2(math.e) * (stored_to_f64(inp.k[base + pos]) @ qh)
+    assert xs.min() > 140.0 and np.all(np.diff(xs) > 0)
+    _say(f"spike {shape}: x in [{xs.min():.1f}, {xs.max():.1f}]")
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), f"spike-{shape}")
+    assert int(pos[-1]) in set(g["sel"][qi].tolist())
