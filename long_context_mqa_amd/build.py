@@ -18,7 +18,12 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhs2.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "attn_chunk.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "hs2_api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_chunk.hip", "score_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip",
+           "hs2_api.cpp"]
+# Kernels whose MFMA results are consumed element by element every tile and that fit in
+# the 256 VGPRs: MFMA destinations in VGPRs instead of accumulator registers (AGPRs),
+# which saves a v_accvgpr_read per result element.
+VGPR_MFMA = {"attn_chunk.hip", "score_bf16.hip"}
 
 
 def hipcc() -> str:
@@ -37,7 +42,8 @@ def common_flags() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"] if src in VGPR_MFMA else []
+    cmd = [hipcc(), *common_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

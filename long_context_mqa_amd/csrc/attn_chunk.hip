@@ -7,14 +7,18 @@
 // 64 query heads share one KV head.
 //
 // The decode-shaped kernels give every query its own K/V stream. When a sequence has
-// many queries, the four waves of a workgroup instead take four consecutive queries of
+// many queries, the eight waves of a workgroup instead take eight consecutive queries of
 // one sequence (a q-tile) and share every K/V tile: each tile is copied once into LDS
-// and multiplied by four queries, which cuts cache traffic per flop by four and makes
-// the pass matrix-bound. Each wave keeps its query's Q in registers and its own online
-// softmax state; the per-tile step is the same as in the decode-shaped pass 1.
+// and multiplied by eight queries, which cuts cache traffic per flop by eight and makes
+// the pass matrix-bound. Two waves share each SIMD, so one wave's softmax (vector ALU)
+// overlaps the other's matrix work. Each wave keeps its own online softmax state and
+// reads its query's Q^T operands from LDS; the per-tile step is the one of the
+// decode-shaped pass 1.
 //   qtile_prep_kernel    lists the q-tiles (never straddling two sequences)
 //   attn_chunk_kernel    pass 1: exact causal attention -> per-split partials
 //   score_chunk_kernel   pass 2: head-summed probabilities + first-digit histograms
+// This file is built with the MFMA results in VGPRs (no accumulator registers): both
+// kernels stay within 256 registers, the budget of two waves per SIMD.
 #include "attn_common.h"
 
 namespace hs2 {
@@ -22,9 +26,13 @@ namespace {
 
 using namespace attn;
 
-constexpr int kQT = kWaves;       // queries per q-tile (one per wave)
-constexpr int kCStages = 3;       // shared LDS stages
-constexpr int kCopiesPerWave = kDmaPerHalf / kWaves;  // 2 of the 8 copies of a tile
+constexpr int kQT = kQTile;                           // queries per q-tile (one per wave)
+constexpr int kCWaves = kQTile;                       // waves per workgroup
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kCStages = 2;                           // shared K+V stages of pass 1
+constexpr int kSStages = 3;                           // shared K stages of the score pass
+constexpr int kCopiesPerWave = kDmaPerHalf / kCWaves; // 1 of the 8 copies of a K or V tile
+static_assert(kCopiesPerWave * kCWaves == kDmaPerHalf, "tile copies must split evenly");
 
 // Raw workgroup barrier for the streaming loops. __syncthreads() carries a memory fence
 // that makes the compiler wait for every vector memory operation it tracks; the loops
@@ -56,8 +64,8 @@ __device__ inline uint32_t excl_scan256(uint32_t v, uint32_t* s_wave, uint32_t& 
   return before + x - v;
 }
 
-// Q-tile list: (first query, count <= 4) per tile, in sequence order; unused entries
-// get count 0. One workgroup.
+// Q-tile list: (first query, count <= kQT) per tile, in sequence order; unused entries
+// get count 0. One workgroup of 256 threads.
 __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles, int max_tiles) {
   __shared__ uint32_t s_wave[4];
   uint32_t off = 0;
@@ -80,16 +88,6 @@ __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles,
   for (uint32_t tix = off + threadIdx.x; tix < (uint32_t)max_tiles; tix += 256) tiles[tix] = make_int2(0, 0);
 }
 
-struct ChunkSmem {
-  union {
-    uint8_t stage[kCStages][2][kTileBytes];  // shared K and V tiles
-    uint8_t q[kQT][kHeads * kDim * 2];       // Q staging before the loop
-  };
-  int tq[kQT];
-  int64_t base[kQT];
-  int redo[kQT];
-};
-
 // Per-wave query of a q-tile; returns false if the wave has no valid query.
 __device__ inline bool tile_query(const SeqsDev& b, int2 td, int wave, int& i, int64_t& base, int& t) {
   i = td.x + wave;
@@ -97,8 +95,22 @@ __device__ inline bool tile_query(const SeqsDev& b, int2 td, int wave, int& i, i
   return query_desc(b, i, base, t);
 }
 
-// Copies this wave's share (2 of 8 wave-wide copies) of the K and V rows of the tile
-// starting at key p0 into one stage. Rows past the last key are clamped.
+// LDS of pass 1: 2 x 16 KB of shared K/V stages and 8 x 16 KB of Q^T operands (160 KB).
+// The per-query scalars live in the stage area before and after the key loop.
+struct ChunkSmem {
+  union {
+    uint8_t stage[kCStages][2][kTileBytes];
+    struct {
+      int tq[kQT];
+      int64_t base[kQT];
+      int redo[kQT];
+    } misc;
+  };
+  uint8_t q[kQT][kHeads * kDim * 2];
+};
+
+// Copies this wave's share (kCopiesPerWave of the 8 wave-wide copies) of the K and V
+// rows of the tile starting at key p0 into one stage. Rows past the last key are clamped.
 __device__ inline void issue_shared(const __bf16* __restrict__ kp, const __bf16* __restrict__ vp, int64_t base,
                                     int p0, int plast, int wave, int lane, uint32_t lk, uint32_t lv) {
 #pragma unroll
@@ -115,8 +127,9 @@ __device__ inline void issue_shared(const __bf16* __restrict__ kp, const __bf16*
 // Streams the tiles of [k0, k1) through the shared stages; every wave issues its share
 // of each tile's copies and takes part in every barrier. Waves with `compute` set run the
 // tile step on the keys their query attends (kMaxOnly: only the logit maximum, into mx).
+// Tile it+1 is copied while tile it is computed.
 template <bool kMaxOnly>
-__device__ inline void chunk_stream(WaveState& st, float (&mx)[2], ChunkSmem& sm, const bf16x8 (&qop)[2][8],
+__device__ inline void chunk_stream(WaveState& st, float (&mx)[2], ChunkSmem& sm, const uint8_t* __restrict__ qs,
                                     bool compute, int t, int k0, int k1, int ntiles, int64_t seq_base,
                                     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp, float c2,
                                     int wave, int lane) {
@@ -126,16 +139,13 @@ __device__ inline void chunk_stream(WaveState& st, float (&mx)[2], ChunkSmem& sm
   uint32_t vb[4];
   vt_bases(lane, vb);
 
-  for (int it = 0; it < min(ntiles, kCStages - 1); ++it)
-    issue_shared(kp, vp, seq_base, k0 + it * kTile, k1 - 1, wave, lane, lk(it), lv(it));
+  if (ntiles > 0) issue_shared(kp, vp, seq_base, k0, k1 - 1, wave, lane, lk(0), lv(0));
   for (int it = 0; it < ntiles; ++it) {
-    const int sidx = it % kCStages;
-    if (it + 1 < ntiles) wait_vmcnt<2 * kCopiesPerWave>(); else wait_vmcnt<0>();
-    loop_barrier();  // every wave's copies of tile it have landed; tile it-1 is released
-    if (it + kCStages - 1 < ntiles) {
-      const int nx = it + kCStages - 1;
-      issue_shared(kp, vp, seq_base, k0 + nx * kTile, k1 - 1, wave, lane, lk(nx % kCStages), lv(nx % kCStages));
-    }
+    const int sidx = it & 1;
+    wait_vmcnt<0>();  // this wave's copies of tile it have landed
+    loop_barrier();   // every wave's copies of tile it have landed; tile it-1 is released
+    if (it + 1 < ntiles)
+      issue_shared(kp, vp, seq_base, k0 + (it + 1) * kTile, k1 - 1, wave, lane, lk(sidx ^ 1), lv(sidx ^ 1));
     const int p0 = k0 + it * kTile;
     if (compute && p0 <= t) {
       bf16x8 kop[8];
@@ -143,14 +153,14 @@ __device__ inline void chunk_stream(WaveState& st, float (&mx)[2], ChunkSmem& sm
       const int nvalid = min(t, k1 - 1) - p0 + 1;  // keys p0 .. p0+nvalid-1 are attended
       const uint32_t vm = __builtin_amdgcn_readfirstlane(nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u));
       if (kMaxOnly)
-        process_tile_max<true>(mx, nullptr, qop, kop, vm, c2, lane);
+        process_tile_max<false>(mx, qs, nullptr, kop, vm, c2, lane);
       else
-        process_tile<true>(st, nullptr, qop, kop, sm.stage[sidx][1], vb, vm, c2, lane);
+        process_tile<false>(st, qs, nullptr, kop, sm.stage[sidx][1], vb, vm, c2, lane);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2* __restrict__ qtiles) {
+__global__ __launch_bounds__(kCThreads) void attn_chunk_kernel(AttnArgs a, const int2* __restrict__ qtiles) {
   __shared__ __align__(16) ChunkSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,17 +172,17 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
   int64_t base;
   const bool mine = tile_query(a.b, td, wave, i, base, t);
   if (lane == 0) {
-    sm.tq[wave] = mine ? t : -1;
-    sm.base[wave] = base;
+    sm.misc.tq[wave] = mine ? t : -1;
+    sm.misc.base[wave] = base;
   }
   __syncthreads();
   int t_max = -1;
   int64_t seq_base = 0;
 #pragma unroll
   for (int w = 0; w < kQT; ++w) {
-    if (sm.tq[w] > t_max) {
-      t_max = sm.tq[w];
-      seq_base = sm.base[w];
+    if (sm.misc.tq[w] > t_max) {
+      t_max = sm.misc.tq[w];
+      seq_base = sm.misc.base[w];
     }
   }
   const int k0 = split * a.split_keys;
@@ -180,23 +190,18 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
   const int k1 = min(t_max + 1, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
 
-  // Q operands of this wave's query, staged through LDS so that no tracked global load
-  // is outstanding inside the streaming loop
-  bf16x8 qop[2][8];
+  // Q^T operands of this wave's query in LDS (read by the tile step), so that the loop
+  // keeps its registers for the accumulators and no tracked global load is outstanding
+  // inside it: 16-byte piece (nb, s, lane) = Q[32nb + l%32][(l/32)*64 + 8s ..]
+  uint8_t* qs = sm.q[wave];
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)(mine ? i : 0) * kHeads * kDim;
-    uint8_t* qs = sm.q[wave];
     for (int e = lane; e < 16 * 64; e += 64) {
       const int ln = e & 63, sidx = (e >> 6) & 7, nb = e >> 9;
-      *reinterpret_cast<uint4*>(qs + e * 16) = *reinterpret_cast<const uint4*>(
+      *reinterpret_cast<bf16x8*>(qs + e * 16) = *reinterpret_cast<const bf16x8*>(
           qp + (32 * nb + (ln & 31)) * kDim + (ln >> 5) * 64 + sidx * 8);
     }
-    __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qop[nb][s] = *reinterpret_cast<const bf16x8*>(qs + ((nb * 8 + s) * 64 + lane) * 16);
-    __syncthreads();  // the staging area becomes the tile stages
+    __syncthreads();  // Q in place; the per-query scalars above have been read
   }
 
   WaveState st;
@@ -205,15 +210,20 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
   const __bf16* kp = static_cast<const __bf16*>(a.k);
   const __bf16* vp = static_cast<const __bf16*>(a.v);
   const int tu = __builtin_amdgcn_readfirstlane(t);  // one query per wave
-  chunk_stream<false>(st, mx, sm, qop, mine, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
+  chunk_stream<false>(st, mx, sm, qs, mine, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
 
   // rare: a wave whose sums overflowed recomputes with its exact logit maximum; the
   // workgroup streams the tiles again together
   const bool bad = mine && !state_finite(st);
-  if (lane == 0) sm.redo[wave] = bad ? 1 : 0;
+  __syncthreads();  // the stage area is free
+  if (lane == 0) sm.misc.redo[wave] = bad ? 1 : 0;
   __syncthreads();
-  if (sm.redo[0] | sm.redo[1] | sm.redo[2] | sm.redo[3]) {
-    chunk_stream<true>(st, mx, sm, qop, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kQT; ++w) any_bad |= sm.misc.redo[w];
+  if (any_bad) {
+    __syncthreads();  // every wave has read the flags before the stages are reused
+    chunk_stream<true>(st, mx, sm, qs, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
     if (bad) {
       state_init(st);
       st.m[0] = mx[0];
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
       st.have_ref = 1;
     }
     __syncthreads();
-    chunk_stream<false>(st, mx, sm, qop, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
+    chunk_stream<false>(st, mx, sm, qs, bad, tu, k0, k1, ntiles, seq_base, kp, vp, a.c2, wave, lane);
   }
 
   if (!mine) return;
@@ -254,23 +264,21 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, const int2*
 // ------------------------------------------------------------------------------------
 // Score pass for q-tiles: S = Q K^T per wave on a shared K tile, the 64-head sum of
 // exp2(x - lse2), written per query, and each query's first-digit histogram in LDS.
-// Scores are staged in LDS and written every kFlush tiles, so that the stores do not
-// interleave with the streaming copies.
+// The histogram packs two 16-bit bin counts per word (the host keeps a split below
+// 2^16 keys). Scores are staged in LDS and written every kFlush tiles, so that the
+// stores do not interleave with the streaming copies.
 // ------------------------------------------------------------------------------------
 constexpr int kFlush = 16;
 
 struct ScoreChunkSmem {
-  union {
-    uint8_t stage[kCStages][kTileBytes];
-    uint8_t q[kQT][kHeads * kDim * 2];
-  };
-  uint32_t hist[kQT][kHistBins];
+  uint8_t stage[kSStages][kTileBytes];
+  uint32_t hist[kQT][kHistBins / 2];
   float sbuf[kQT][kFlush * kTile];
   int tq[kQT];
   int64_t base[kQT];
 };
 
-__global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int2* __restrict__ qtiles) {
+__global__ __launch_bounds__(kCThreads) void score_chunk_kernel(ScoreArgs a, const int2* __restrict__ qtiles) {
   __shared__ __align__(16) ScoreChunkSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,7 +295,7 @@ __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int
     sm.tq[wave] = mine ? nc : 0;
     sm.base[wave] = base;
   }
-  for (int e = lane; e < kHistBins; e += 64) sm.hist[wave][e] = 0u;
+  for (int e = lane; e < kHistBins / 2; e += 64) sm.hist[wave][e] = 0u;
   __syncthreads();
   int nc_max = 0;
   int64_t seq_base = 0;
@@ -303,27 +311,23 @@ __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int
   const int k1 = min(nc_max, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
 
+  // Q operands in registers (S = Q K^T: Q is the A operand, heads as rows) and the
+  // per-head log2-domain LSE in the C layout; the barrier below waits for the loads
   bf16x8 qop[2][8];
   float l2[2][16];
   const int hrow = 4 * (lane >> 5);
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)(mine ? i : 0) * kHeads * kDim;
-    uint8_t* qs = sm.q[wave];
-    for (int e = lane; e < 16 * 64; e += 64) {
-      const int ln = e & 63, sidx = (e >> 6) & 7, mb = e >> 9;
-      *reinterpret_cast<uint4*>(qs + e * 16) = *reinterpret_cast<const uint4*>(
-          qp + (32 * mb + (ln & 31)) * kDim + (ln >> 5) * 64 + sidx * 8);
-    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qop[mb][s] = *reinterpret_cast<const bf16x8*>(qp + (32 * mb + (lane & 31)) * kDim + (lane >> 5) * 64 + s * 8);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         l2[mb][j] = mine ? a.lse2[(size_t)i * kHeads + 32 * mb + 8 * (j >> 2) + hrow + (j & 3)] : 0.0f;
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qop[mb][s] = *reinterpret_cast<const bf16x8*>(qs + ((mb * 8 + s) * 64 + lane) * 16);
     __syncthreads();
   }
 
@@ -349,12 +353,12 @@ __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int
     }
   };
 
-  for (int it = 0; it < min(ntiles, kCStages - 1); ++it) issue_k(it, lk(it));
+  for (int it = 0; it < min(ntiles, kSStages - 1); ++it) issue_k(it, lk(it));
   for (int it = 0; it < ntiles; ++it) {
-    const int sidx = it % kCStages;
+    const int sidx = it % kSStages;
     if (it + 1 < ntiles) wait_vmcnt<kCopiesPerWave>(); else wait_vmcnt<0>();
     loop_barrier();
-    if (it + kCStages - 1 < ntiles) issue_k(it + kCStages - 1, lk((it + kCStages - 1) % kCStages));
+    if (it + kSStages - 1 < ntiles) issue_k(it + kSStages - 1, lk((it + kSStages - 1) % kSStages));
     const int p0 = k0 + it * kTile;
     if (mine && p0 < nc) {
       bf16x8 kc[8];
@@ -370,13 +374,14 @@ __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sum += fast_exp2(acc[mb][j] * a.c2 - l2[mb][j]);
+        for (int j = 0; j < 16; ++j) sum += fast_exp2(fmaf(acc[mb][j], a.c2, -l2[mb][j]));
       const float other = __shfl_xor(sum, 32);
       const float total = (lane < 32) ? sum + other : other + sum;
       const int p = p0 + (lane & 31);
       if (lane < 32 && p < min(k1, nc)) {
         sm.sbuf[wave][(it % kFlush) * kTile + lane] = total;
-        atomicAdd(&sm.hist[wave][__float_as_uint(total) >> kHistShift], 1u);
+        const uint32_t bin = __float_as_uint(total) >> kHistShift;
+        atomicAdd(&sm.hist[wave][bin >> 1], 1u << (16 * (bin & 1)));
       }
     }
     if (mine && ((it + 1) % kFlush == 0 || it + 1 == ntiles)) {
@@ -387,9 +392,10 @@ __global__ __launch_bounds__(256) void score_chunk_kernel(ScoreArgs a, const int
   __syncthreads();
   if (!mine) return;
   uint32_t* hq = a.hist + (size_t)i * kHistBins;
-  for (int e = lane; e < kHistBins; e += 64) {
+  for (int e = lane; e < kHistBins / 2; e += 64) {
     const uint32_t c = sm.hist[wave][e];
-    if (c) atomicAdd(&hq[e], c);
+    if (c & 0xffffu) atomicAdd(&hq[2 * e], c & 0xffffu);
+    if (c >> 16) atomicAdd(&hq[2 * e + 1], c >> 16);
   }
 }
 
@@ -401,12 +407,12 @@ hipError_t launch_qtile_prep(const SeqsDev& b, int2* tiles, int max_tiles, hipSt
 }
 
 hipError_t launch_attn_chunk(const AttnArgs& a, const int2* tiles, int max_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(attn_chunk_kernel, dim3(max_tiles * a.n_split), dim3(256), 0, s, a, tiles);
+  hipLaunchKernelGGL(attn_chunk_kernel, dim3(max_tiles * a.n_split), dim3(kCThreads), 0, s, a, tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(score_chunk_kernel, dim3(max_tiles * a.n_split), dim3(256), 0, s, a, tiles);
+  hipLaunchKernelGGL(score_chunk_kernel, dim3(max_tiles * a.n_split), dim3(kCThreads), 0, s, a, tiles);
   return hipGetLastError();
 }
 

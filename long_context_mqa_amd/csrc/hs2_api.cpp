@@ -1,6 +1,7 @@
 // Host entry points of libhs2: argument checks, workspace planning and kernel launches.
 // Every check runs before anything is enqueued; the library allocates nothing.
 #include <cmath>
+#include <limits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -87,18 +88,20 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
   const int64_t max_cand = std::max<int64_t>(0, (int64_t)b->max_kv_len - window + 1);
   p.chunk = dt == HS2_BF16 && b->max_q_per_seq >= kChunkMinQueries;
   if (p.chunk) {
-    // q-tiles of kWaves queries of one sequence; splits fill one round of workgroups
-    p.max_tiles = (int)(tq / kWaves + b->num_seqs + 1);
+    // q-tiles of kQTile queries of one sequence; splits fill one round of workgroups.
+    // A score split stays below 2^16 keys (the kernel's 16-bit LDS bin counts).
+    p.max_tiles = (int)(tq / kQTile + b->num_seqs + 1);
     const int64_t want = std::max<int64_t>(1, kTargetGroups / std::max(1, p.max_tiles));
-    auto split_of = [&](int64_t keys) {
+    auto split_of = [&](int64_t keys, int64_t cap) {
       Split sp;
       if (keys <= 0) return Split{1, kTile};
-      sp.split_keys = (int)(ceil_div(ceil_div(keys, std::min<int64_t>(want, kMaxSplit)), kTile) * kTile);
+      sp.split_keys = (int)std::min<int64_t>(
+          ceil_div(ceil_div(keys, std::min<int64_t>(want, kMaxSplit)), kTile) * kTile, cap);
       sp.n_split = (int)ceil_div(keys, sp.split_keys);
       return sp;
     };
-    p.attn = split_of(b->max_kv_len);
-    p.score = split_of(max_cand);
+    p.attn = split_of(b->max_kv_len, std::numeric_limits<int>::max());
+    p.score = split_of(max_cand, kScoreSplitMax);
   } else {
     p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
     p.score = plan_split(launch_work(b, max_cand), max_cand);

@@ -18,6 +18,8 @@ constexpr int kHistBits = 12;  // first radix digit: bits 30..19 of a non-negati
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 31 - kHistBits;
 constexpr int kCandCap = 4096; // threshold-bin candidates kept per query for the in-LDS select
+constexpr int kQTile = 8;      // queries per q-tile of the chunked selector (one wave each)
+constexpr int kScoreSplitMax = 32768;  // keys per chunked score workgroup (16-bit LDS bin counts)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -1,0 +1,126 @@
+// Selection score pass (pass 2) of the decode-shaped selector for gfx950: the per-key
+// sum over the 64 heads of the softmax probability, from the exact log-sum-exp of pass 1.
+//
+// Method (page title and section): arex-research.com, "Xiaomi MiMo lead Luo Fuli
+// publishes the MiMo-V3 core architecture HySparse2", section "Outer KV Bridging, inner
+// KV Reuse": the full-attention layer's scores select the keys the sparse layers attend.
+//
+// Built with the MFMA results in VGPRs (no accumulator registers): the loop needs about
+// 180 registers, and the softmax reads every result element once per tile.
+#include "attn_common.h"
+
+namespace hs2 {
+namespace {
+
+using namespace attn;
+
+// ------------------------------------------------------------------------------------
+// Selection score pass: score_j = sum_h exp2(x_hj - lse2_h) for candidates j <= t-window,
+// written per query, plus a histogram of the first radix digit (bits 30..19).
+// S = Q K^T here (heads as rows): each lane sums its 32 head values of one key, and one
+// exchange with lane l^32 completes the 64-head sum. K tiles stream through kScoreStages
+// per-wave LDS stages (same swizzled layout and DMA as pass 1).
+// ------------------------------------------------------------------------------------
+constexpr int kScoreStages = 4;
+
+struct ScoreSmem {
+  uint8_t stage[kWaves][kScoreStages][kTileBytes];
+  uint32_t hist[kHistBins];
+};
+
+__global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
+  __shared__ __align__(16) ScoreSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x / a.n_split;
+  const int split = blockIdx.x - i * a.n_split;
+  int64_t base;
+  int t;
+  if (!query_desc(a.b, i, base, t)) return;
+  const int nc = max(0, t - a.window + 1);
+  if (nc <= a.top_k) return;
+  const int k0 = split * a.split_keys;
+  if (k0 >= nc) return;
+  const int k1 = min(nc, k0 + a.split_keys);
+  const int ntiles = (k1 - k0 + kTile - 1) / kTile;
+
+  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) sm.hist[e] = 0u;
+
+  bf16x8 qop[2][8];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)i * kHeads * kDim;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qop[mb][s] = *reinterpret_cast<const bf16x8*>(qp + (32 * mb + (lane & 31)) * kDim +
+                                                      (lane >> 5) * 64 + s * 8);
+  }
+  float l2[2][16];
+  const int hrow = 4 * (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      l2[mb][j] = a.lse2[(size_t)i * kHeads + 32 * mb + 8 * (j >> 2) + hrow + (j & 3)];
+  __syncthreads();  // histogram cleared; the loads above have completed
+
+  const __bf16* kp = static_cast<const __bf16*>(a.k);
+  float* srow = a.scores + (size_t)i * a.score_stride;
+  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  uint32_t lk[kScoreStages];
+#pragma unroll
+  for (int sidx = 0; sidx < kScoreStages; ++sidx)
+    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx]);
+  auto issue = [&](int it, uint32_t lds) {
+    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
+    const int rel = p < k1 ? p : 0;
+    issue_rows<true>(kp, base, rel, lane, lds);
+  };
+  for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, lk[it]);
+  for (int it = 0; it < ntw; ++it) {
+    const int sidx = it % kScoreStages;
+    // K(it) has landed once at most the groups issued after it are outstanding (score
+    // stores issued meanwhile only make this wait longer, never shorter)
+    const int later = min(ntw, it + kScoreStages) - (it + 1);
+    wait_vmcnt_dyn(later * kDmaPerHalf);
+    bf16x8 kc[8];
+    read_k(sm.stage[wave][sidx], lane, kc);
+    if (it + kScoreStages < ntw) issue(it + kScoreStages, lk[sidx]);
+    f32x16 acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      acc[mb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc[mb] = mfma(qop[mb][s], kc[s], acc[mb]);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += fast_exp2(acc[mb][j] * a.c2 - l2[mb][j]);
+    // lane l and l^32 hold complementary heads of the same key; add in a fixed order
+    const float other = __shfl_xor(sum, 32);
+    const float total = (lane < 32) ? sum + other : other + sum;
+    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
+    if (lane < 32 && p < k1) {
+      srow[p] = total;
+      atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* hq = a.hist + (size_t)i * kHistBins;
+  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) {
+    const uint32_t c = sm.hist[e];
+    if (c) atomicAdd(&hq[e], c);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(score_bf16_kernel, dim3(a.b.total_q * a.n_split), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs2
