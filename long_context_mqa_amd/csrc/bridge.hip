@@ -10,11 +10,14 @@
 //
 // The 2L projection matrices are treated as one [d_model x 128*2L] right-hand side. The
 // weights are first transposed into the workspace (k contiguous), so that both MFMA
-// operands read 16 contiguous bytes per lane. Each workgroup computes a 256-row x
-// 256-column tile of C^T = W^T H^T (two output matrices) with four waves of 128 x 128
-// (accumulators in the AGPRs); operand tiles stream through three LDS stages by
-// direct-to-LDS loads. Tiles of the same rows run back to back on one XCD, so H is read
-// from HBM once and re-served from that XCD's L2 for the other column tiles.
+// operands read 16 contiguous bytes per lane. Each workgroup computes a tile of 256 rows
+// x 384 columns (three output matrices; 256 when 2L is not a multiple of 3) of
+// C^T = W^T H^T with eight waves, two per SIMD, of 64 rows x 192 (128) columns. The
+// wider tile re-reads each H row 2L/3 times instead of L times and moves 17% fewer
+// operand bytes per MFMA; the tile's 192 accumulator registers per lane still allow two
+// waves per SIMD. Operand tiles stream through three LDS stages by direct-to-LDS loads.
+// Tiles of the same rows run back to back on one XCD, so H is read from HBM once and
+// re-served from that XCD's L2 for the other column tiles.
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -24,8 +27,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;   // H rows per workgroup
-constexpr int kBN = 256;   // output columns per workgroup (two matrices of 128)
 constexpr int kXcds = 8;
+constexpr int kGWaves = 8;
 
 struct WPtrs {
   const uint16_t* w[16];
@@ -50,24 +53,35 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(WPtrs wp, uint16_t* wt
 
 constexpr int kStagesG = 3;      // LDS stages of the contraction loop
 constexpr int kKStep = 32;       // contraction step (two MFMA k-steps of 16)
-constexpr int kTileB = 256 * kKStep * 2;  // 16 KB: one 256 x 32 bf16 operand tile
 
-// Operand tiles in LDS: 256 rows of 64 bytes (32 bf16 of the contraction); the 16-byte
-// chunk c of row r sits at chunk position c ^ ((r >> 2) & 3), so that the eight lanes an
-// LDS read serves together (eight consecutive rows, same chunk) hit distinct banks.
+// Operand tiles in LDS: rows of 64 bytes (32 bf16 of the contraction); the 16-byte chunk
+// c of row r sits at chunk position c ^ ((r >> 2) & 3), so that the eight lanes an LDS
+// read serves together (eight consecutive rows, same chunk) hit distinct banks.
 __device__ inline uint32_t op_off(int row, int chunk) {
   return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
 }
 
-struct GemmSmem {
-  uint8_t a[kStagesG][kTileB];  // transposed weights: [n][k]
-  uint8_t b[kStagesG][kTileB];  // hidden states:      [row][k]
-};
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
-__global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeArgs a) {
-  __shared__ __align__(16) GemmSmem sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_nt = a.n_mats / 2;
+// kCols output columns per workgroup (256 or 384). Wave w: rows 64*(w%4) .. +63 of the
+// tile, columns (kCols/2)*(w/4) .. + kCols/2 - 1, as kXB x 2 blocks of 32 x 32.
+template <int kCols>
+__global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a) {
+  constexpr int kTA = kCols * kKStep * 2;        // W^T tile bytes per stage
+  constexpr int kTB = kBM * kKStep * 2;          // H tile bytes per stage
+  constexpr int kCopA = kCols / 16 / kGWaves;    // 1 KB copies per wave per stage (16 rows each)
+  constexpr int kCopB = kBM / 16 / kGWaves;
+  constexpr int kGroup = kCopA + kCopB;          // copies issued per wave per stage
+  constexpr int kXB = kCols / 64;                // 32-column blocks per wave
+  static_assert(kCopA * 16 * kGWaves == kCols && kCopB * 16 * kGWaves == kBM, "copies must split evenly");
+  __shared__ __align__(16) uint8_t lds_a[kStagesG][kTA];
+  __shared__ __align__(16) uint8_t lds_b[kStagesG][kTB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_nt = a.n_mats * kDim / kCols;
   const int64_t n_rt = (a.n_rows + kBM - 1) / kBM;
   // XCD-aware order: workgroup b runs on XCD b % 8; consecutive slots of one XCD take
   // the column tiles of one row tile, so the H rows are re-read from that XCD's L2.
@@ -77,85 +91,88 @@ __global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeArgs a) {
   const int nt = slot % n_nt;
   if (rt >= n_rt) return;
   const int64_t r0 = rt * kBM;
-  const uint16_t* wt = a.wt + (size_t)nt * kBN * a.d_model;
-  const int wr = wave & 1;   // 128-row half
-  const int wn = wave >> 1;  // 128-column half (one output matrix)
+  const uint16_t* wt = a.wt + (size_t)nt * kCols * a.d_model;
+  const int wr = wave & 3;   // 64-row quarter
+  const int wc = wave >> 2;  // column half
 
-  const uint32_t la0 = (uint32_t)(size_t)sm.a[0];
-  const uint32_t lb0 = (uint32_t)(size_t)sm.b[0];
-  // this wave's copy rows: copies r = 4*wave .. 4*wave+3 cover rows 16r .. 16r+15
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
+  const uint32_t la0 = (uint32_t)(size_t)lds_a[0];
+  const uint32_t lb0 = (uint32_t)(size_t)lds_b[0];
+  // this wave's copies: A copies kCopA*wave + q, B copies kCopB*wave + q, 16 rows each
+  const uint16_t* ga[kCopA];
+  const uint16_t* gb[kCopB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 4 * wave + q;
-    const int row = 16 * r + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    ga[q] = wt + (size_t)row * a.d_model + chunk * 8;
+  for (int q = 0; q < kCopA; ++q) {
+    const int row = 16 * (kCopA * wave + q) + (lane >> 2);
+    ga[q] = wt + (size_t)row * a.d_model + ((lane & 3) ^ ((row >> 2) & 3)) * 8;
+  }
+#pragma unroll
+  for (int q = 0; q < kCopB; ++q) {
+    const int row = 16 * (kCopB * wave + q) + (lane >> 2);
     int64_t hr = r0 + row;
     if (hr >= a.n_rows) hr = a.n_rows - 1;
-    gb[q] = a.h + hr * a.d_model + chunk * 8;
+    gb[q] = a.h + hr * a.d_model + ((lane & 3) ^ ((row >> 2) & 3)) * 8;
   }
   auto issue = [&](int kt, int st) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 4 * wave + q;
-      dma16(ga[q] + kt * kKStep, __builtin_amdgcn_readfirstlane(la0 + st * kTileB + r * 1024));
-      dma16(gb[q] + kt * kKStep, __builtin_amdgcn_readfirstlane(lb0 + st * kTileB + r * 1024));
-    }
+    for (int q = 0; q < kCopA; ++q)
+      dma16(ga[q] + kt * kKStep, la0 + st * kTA + (kCopA * wave + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < kCopB; ++q)
+      dma16(gb[q] + kt * kKStep, lb0 + st * kTB + (kCopB * wave + q) * 1024);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kXB][2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < kXB; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
 
-  const int KT = a.d_model / kKStep;
+  const int KT = a.d_model / kKStep;  // >= 2 (d_model is a multiple of 64)
   issue(0, 0);
-  if (KT > 1) issue(1, 1);
+  issue(1, 1);
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % kStagesG;
-    // this wave's 8 copies of stage kt have landed once only those of stage kt+1 remain
-    if (kt + 1 < KT)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // the whole stage has landed; stage kt-1 is no longer read
+    // this wave's copies of stage kt have landed once only those of stage kt+1 remain
+    if (kt + 1 < KT) wait_vm<kGroup>(); else wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // the whole stage has landed; stage kt-1 is no longer read
     if (kt + 2 < KT) issue(kt + 2, (kt + 2) % kStagesG);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = 2 * ks + (lane >> 5);
-      bf16x8 av[4], bv[4];
+      bf16x8 av[kXB], bv[2];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        av[x] = *reinterpret_cast<const bf16x8*>(sm.a[st] + op_off(wn * 128 + 32 * x + (lane & 31), c));
-        bv[x] = *reinterpret_cast<const bf16x8*>(sm.b[st] + op_off(wr * 128 + 32 * x + (lane & 31), c));
-      }
+      for (int x = 0; x < kXB; ++x)
+        av[x] = *reinterpret_cast<const bf16x8*>(lds_a[st] + op_off(wc * (kCols / 2) + 32 * x + (lane & 31), c));
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 2; ++y)
+        bv[y] = *reinterpret_cast<const bf16x8*>(lds_b[st] + op_off(wr * 64 + 32 * y + (lane & 31), c));
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+      for (int x = 0; x < kXB; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
   }
 
   // C^T[n][row]: lane holds rows 32*y + l%32, columns 32*x + 8*(j/4) + 4*(l/32) + j%4
-  uint16_t* out = a.outs[2 * nt + wn];
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int64_t grow = r0 + wr * 128 + 32 * y + (lane & 31);
+  for (int y = 0; y < 2; ++y) {
+    const int64_t grow = r0 + wr * 64 + 32 * y + (lane & 31);
     if (grow >= a.n_rows) continue;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < kXB; ++x) {
+      const int gc = nt * kCols + wc * (kCols / 2) + 32 * x;  // first output column of the block
+      uint16_t* out = a.outs[gc / kDim];
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int n0 = 32 * x + 8 * jg + 4 * (lane >> 5);
+        const int n0 = gc % kDim + 8 * jg + 4 * (lane >> 5);
         __bf16 v4[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v4[q] = (__bf16)acc[x][y][4 * jg + q];
         *reinterpret_cast<uint2*>(out + grow * kDim + n0) = __builtin_bit_cast(uint2, v4);
       }
+    }
   }
 }
 
@@ -173,8 +190,13 @@ hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w
 hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s) {
   const int64_t n_rt = (a.n_rows + kBM - 1) / kBM;
   const int64_t per_xcd = (n_rt + kXcds - 1) / kXcds;
-  const int64_t grid = per_xcd * kXcds * (a.n_mats / 2);
-  hipLaunchKernelGGL(bridge_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.n_mats % 3 == 0) {
+    const int64_t grid = per_xcd * kXcds * (a.n_mats * kDim / 384);
+    hipLaunchKernelGGL(bridge_gemm_kernel<384>, dim3((unsigned)grid), dim3(64 * kGWaves), 0, s, a);
+  } else {
+    const int64_t grid = per_xcd * kXcds * (a.n_mats * kDim / 256);
+    hipLaunchKernelGGL(bridge_gemm_kernel<256>, dim3((unsigned)grid), dim3(64 * kGWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -249,6 +249,16 @@ def test_bridge_small_ragged_rows():
     _bridge_check(bi, gk, gv, np.arange(1000))
 
 
+@pytest.mark.parametrize("n_layers", [2, 6])
+def test_bridge_layer_counts(n_layers):
+    """Both column tilings of the fan-out kernel: 2L = 4 matrices (256-column tiles) and
+    2L = 12 (four 384-column tiles, each spanning three output matrices)."""
+    bi = make_bridge_inputs(600, n_layers=n_layers, seed=23 + n_layers)
+    gk, gv = hs2.bridge_kv(to_dev(bi.h), [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v])
+    _say(f"bridge {n_layers} layers")
+    _bridge_check(bi, gk, gv, np.arange(600))
+
+
 def test_bridge_one_layer_and_tiny_rows():
     bi = make_bridge_inputs(37, n_layers=1, seed=22, d_model=256)
     gk, gv = hs2.bridge_kv(to_dev(bi.h), [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v])
