@@ -87,6 +87,11 @@ typedef struct hs2_seqs {
   int32_t max_kv_len;      /* host: an upper bound of every kv_len                         */
   int64_t total_kv_rows;   /* host: rows of K and V                                        */
   int32_t max_q_per_seq;   /* host: an upper bound of the queries of any one sequence      */
+  const int32_t* kv_len_host; /* host, nullable: a copy of kv_len. Used only to size the
+                              split of each query's keys over workgroups when every
+                              sequence has at most one query (ragged decode); without it
+                              the split assumes equal lengths, which may leave a second,
+                              mostly idle round of workgroups                            */
 } hs2_seqs;
 
 /* Library version: HS2_VERSION of the built library. */
@@ -136,7 +141,9 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
  *   sel_idx  device [total_q][top_k] int32 (may be NULL when top_k == 0)
  *   sel_count device [total_q] int32 = min(top_k, candidates), or NULL
  *   workspace device scratch of at least hs2_full_attn_select_workspace_size(...) bytes,
- *            256-byte aligned; its contents on entry do not matter.
+ *            256-byte aligned; its contents on entry do not matter. The size depends on
+ *            the descriptor's host fields (kv_len_host included): query it with the
+ *            descriptor that the call will use.
  * ------------------------------------------------------------------------------------ */
 size_t hs2_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_heads,
                                            int32_t head_dim, int32_t window, int32_t top_k,

@@ -109,13 +109,13 @@ __device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem& sm,
 }
 
 template <bool kGather>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, uint32_t* hist,
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, WorkList wl, uint32_t* hist,
                                                         uint32_t* counters) {
   __shared__ __align__(16) AttnSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - i * a.n_split;
+  int i, split;
+  work_item(wl, a.n_split, i, split);
   const int k0 = split * a.split_keys;
 
   // Loads that do not depend on the query's position go out first: the gathered slots
@@ -395,12 +395,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
+hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
                             uint32_t* counters, hipStream_t s) {
   if (gather)
-    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(256), 0, s, a, hist, counters);
+    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(256), 0, s, a, hist, counters);
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
   return hipGetLastError();
 }
 

@@ -63,6 +63,52 @@ Split plan_split(int64_t work, int64_t max_keys) {
   return s;
 }
 
+// Split of ragged single-query sequences from their host lengths: the smallest split
+// (a multiple of one tile) whose active workgroups, sum over sequences of
+// ceil(keys_s / split), fit one round of kTargetGroups; or two rounds, if their total is
+// at least 10% shorter (each round adds its own prologue, merge and partial writes).
+// keys_s = n_s - sub (clamped at 0).
+bool plan_split_lengths(const hs2_seqs* b, int64_t sub, int64_t max_keys, Split& out, WorkList* wl) {
+  if (!b->kv_len_host || b->max_q_per_seq > 1 || max_keys <= 0) return false;
+  auto active = [&](int64_t sk) {
+    int64_t n = 0;
+    for (int s = 0; s < b->num_seqs; ++s) {
+      const int64_t k = std::max<int64_t>(0, (int64_t)b->kv_len_host[s] - sub);
+      n += ceil_div(k, sk);
+    }
+    return n;
+  };
+  const int64_t hi_tiles = ceil_div(max_keys, kTile);
+  const int64_t lo_tiles = std::max<int64_t>(1, ceil_div(hi_tiles, kMaxSplit));  // the combine's bound
+  auto smallest = [&](int64_t cap) {  // smallest split (in tiles) with at most cap active groups
+    int64_t lo = lo_tiles, hi = hi_tiles;
+    if (active(hi * kTile) > cap) return (int64_t)-1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (active(mid * kTile) <= cap) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  int64_t best = smallest(kTargetGroups);
+  const int64_t two = smallest(2 * kTargetGroups);
+  if (best < 0 || (two > 0 && 20 * two < 9 * best)) best = two;
+  if (best < 0) return false;
+  out.split_keys = (int)(best * kTile);
+  out.n_split = (int)ceil_div(max_keys, out.split_keys);
+  // the active (query, split) pairs, when query s is the one query of sequence s
+  if (wl) {
+    wl->n = 0;
+    if (b->total_q == b->num_seqs && active(out.split_keys) <= kMaxWorkItems && out.n_split <= 512) {
+      for (int q = 0; q < b->num_seqs; ++q) {
+        const int64_t k = std::max<int64_t>(0, (int64_t)b->kv_len_host[q] - sub);
+        const int64_t ns = ceil_div(k, out.split_keys);
+        for (int64_t sp = 0; sp < ns; ++sp) wl->item[wl->n++] = ((uint32_t)q << 9) | (uint32_t)sp;
+      }
+    }
+  }
+  return true;
+}
+
 // Keys processed by one launch: every query over up to max_keys, bounded for ragged
 // single-query sequences by the rows of the batch.
 int64_t launch_work(const hs2_seqs* b, int64_t max_keys) {
@@ -73,6 +119,7 @@ int64_t launch_work(const hs2_seqs* b, int64_t max_keys) {
 
 struct SelectPlan {
   bool chunk = false;     // many queries per sequence: q-tile kernels sharing K/V tiles
+  WorkList attn_wl{}, score_wl{};  // bf16 decode path with host lengths: the active pairs
   int max_tiles = 0;      // q-tiles launched (upper bound of the tiles of the batch)
   size_t off_tiles = 0;
   Split attn, score;
@@ -103,8 +150,11 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
     p.attn = split_of(b->max_kv_len, std::numeric_limits<int>::max());
     p.score = split_of(max_cand, kScoreSplitMax);
   } else {
-    p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
-    p.score = plan_split(launch_work(b, max_cand), max_cand);
+    const bool lists = dt == HS2_BF16;
+    if (!plan_split_lengths(b, 0, b->max_kv_len, p.attn, lists ? &p.attn_wl : nullptr))
+      p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
+    if (!plan_split_lengths(b, window - 1, max_cand, p.score, lists ? &p.score_wl : nullptr))
+      p.score = plan_split(launch_work(b, max_cand), max_cand);
   }
   p.f_split = (int)std::max<int64_t>(1, ceil_div(max_cand, kFilterLen));
   p.score_stride = (max_cand + 63) / 64 * 64;
@@ -310,7 +360,8 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     if (p.chunk)
       e = launch_attn_chunk(a, tiles, p.max_tiles, s);
     else
-      e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s) : launch_attn_bf16(a, false, grid, hist, counters, s);
+      e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s)
+              : launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
   }
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "full attention launch");
@@ -366,7 +417,7 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
       if (p.chunk)
         e = launch_score_chunk(sc, tiles, p.max_tiles, s);
       else
-        e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, s);
+        e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, p.score_wl, s);
     }
     if (e == hipSuccess) e = mk.after(2);
     if (e != hipSuccess) return hip_fail(e, "score launch");
@@ -428,7 +479,8 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
   LaunchMarks mk(s);
   hipError_t e = mk.before(0);
   if (e == hipSuccess)
-    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s) : launch_attn_bf16(a, true, grid, nullptr, nullptr, s);
+    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
+            : launch_attn_bf16(a, WorkList{}, true, grid, nullptr, nullptr, s);
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   if (p.attn.n_split > 1) {

@@ -63,6 +63,26 @@ struct AttnArgs {
   float* lse2;            // [total_q][64] log2 domain, nullable (n_split == 1)
 };
 
+// (query, split) pairs of a launch in launch order: workgroup b takes item b, so that the
+// active pairs fill the XCDs (b % 8) evenly and no workgroup is launched without work.
+// n == 0: the grid is total_q x n_split in query-major order.
+constexpr int kMaxWorkItems = 512;
+struct WorkList {
+  int32_t n;
+  uint32_t item[kMaxWorkItems];  // query << 9 | split (split < 512)
+};
+
+__device__ inline void work_item(const WorkList& wl, int n_split, int& i, int& split) {
+  if (wl.n > 0) {
+    const uint32_t it = wl.item[blockIdx.x];
+    i = (int)(it >> 9);
+    split = (int)(it & 511u);
+  } else {
+    i = blockIdx.x / n_split;
+    split = blockIdx.x - i * n_split;
+  }
+}
+
 struct CombineArgs {
   SeqsDev b;
   const Partial* part;
@@ -170,7 +190,7 @@ __device__ inline int logical_keys(bool gather, int t, int window, int top_k) {
 // ---------------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------------
-hipError_t launch_attn_bf16(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
+hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
                             uint32_t* counters, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
                            uint32_t* counters, hipStream_t s);
@@ -178,7 +198,7 @@ hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
 hipError_t launch_qtile_prep(const SeqsDev& b, int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_attn_chunk(const AttnArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
-hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_score_bf16(const ScoreArgs& a, const WorkList& wl, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s);

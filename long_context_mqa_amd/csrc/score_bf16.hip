@@ -28,12 +28,12 @@ struct ScoreSmem {
   uint32_t hist[kHistBins];
 };
 
-__global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
   __shared__ __align__(16) ScoreSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - i * a.n_split;
+  int i, split;
+  work_item(wl, a.n_split, i, split);
   int64_t base;
   int t;
   if (!query_desc(a.b, i, base, t)) return;
@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a) {
 
 }  // namespace
 
-hipError_t launch_score_bf16(const ScoreArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(score_bf16_kernel, dim3(a.b.total_q * a.n_split), dim3(256), 0, s, a);
+hipError_t launch_score_bf16(const ScoreArgs& a, const WorkList& wl, hipStream_t s) {
+  const int grid = wl.n > 0 ? wl.n : a.b.total_q * a.n_split;
+  hipLaunchKernelGGL(score_bf16_kernel, dim3(grid), dim3(256), 0, s, a, wl);
   return hipGetLastError();
 }
 

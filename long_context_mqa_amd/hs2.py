@@ -9,6 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
 
 import torch
 
@@ -43,6 +46,7 @@ class hs2_seqs(ctypes.Structure):
         ("max_kv_len", ctypes.c_int32),
         ("total_kv_rows", ctypes.c_int64),
         ("max_q_per_seq", ctypes.c_int32),
+        ("kv_len_host", ctypes.c_void_p),
     ]
 
 
@@ -122,11 +126,17 @@ class Batch:
     max_kv_len: int
     total_kv_rows: int
     max_q_per_seq: int
+    kv_len_host: Optional[np.ndarray] = None   # int32 [S], contiguous: balances the key split
 
     def c(self) -> hs2_seqs:
+        kh = None
+        if self.kv_len_host is not None:
+            assert self.kv_len_host.dtype == np.int32 and self.kv_len_host.flags["C_CONTIGUOUS"]
+            assert self.kv_len_host.size == self.kv_start.numel()
+            kh = self.kv_len_host.ctypes.data
         return hs2_seqs(int(self.kv_start.numel()), _ptr(self.kv_start), _ptr(self.kv_len), _ptr(self.q_start),
                         _ptr(self.q_pos), int(self.total_q), int(self.max_kv_len), int(self.total_kv_rows),
-                        int(self.max_q_per_seq))
+                        int(self.max_q_per_seq), kh)
 
     @staticmethod
     def from_host(kv_start, kv_len, q_start, q_pos, total_kv_rows: int, device="cuda") -> "Batch":
@@ -138,7 +148,8 @@ class Batch:
         per = (qs[1:] - qs[:-1]) if qs.numel() > 1 else torch.zeros(1, dtype=torch.int32)
         return Batch(ks.to(device), kl.to(device), qs.to(device), qp.to(device), int(qp.numel()),
                      max(1, int(kl.max().item()) if kl.numel() else 1), int(total_kv_rows),
-                     int(per.max().item()) if per.numel() else 0)
+                     int(per.max().item()) if per.numel() else 0,
+                     np.ascontiguousarray(kl.numpy(), dtype=np.int32))
 
 
 def full_attn_select_workspace_size(batch: Batch, window: int, top_k: int, dtype=torch.bfloat16) -> int:

@@ -121,3 +121,18 @@ def test_workspace_sizes_grow_with_the_batch(lib):
     # scores of every candidate of every query fit
     assert g >= 64 * (131072 - 127) * 4
     assert lib.hs2_full_attn_select_workspace_size(None, 64, 128, 128, 1024, 0) == 0
+
+
+def test_workspace_sizes_follow_host_lengths(lib):
+    """Ragged single-query batches with a host copy of the lengths are planned from those
+    lengths: the selector's workspace (per-split partials) differs from the equal-length
+    plan, and both sizes are positive and 256-byte multiples."""
+    import numpy as np
+    lens = np.array([4096, 6000, 300000, 510000, 9000, 120000] * 5, dtype=np.int32)
+    b0 = hs2.hs2_seqs(len(lens), FAKE, FAKE, FAKE, FAKE, len(lens), int(lens.max()), int(lens.sum()), 1)
+    b1 = hs2.hs2_seqs(len(lens), FAKE, FAKE, FAKE, FAKE, len(lens), int(lens.max()), int(lens.sum()), 1,
+                      lens.ctypes.data)
+    s0 = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b0), 64, 128, 128, 1024, hs2.HS2_BF16)
+    s1 = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b1), 64, 128, 128, 1024, hs2.HS2_BF16)
+    assert s0 > 0 and s1 > 0 and s0 % 256 == 0 and s1 % 256 == 0
+    assert s0 != s1
