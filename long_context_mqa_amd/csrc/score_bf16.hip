@@ -23,9 +23,12 @@ using namespace attn;
 // ------------------------------------------------------------------------------------
 constexpr int kScoreStages = 4;
 
+constexpr int kSFlush = 32;  // tiles of scores staged per wave before they are written
+
 struct ScoreSmem {
   uint8_t stage[kWaves][kScoreStages][kTileBytes];
   uint32_t hist[kHistBins];
+  float sbuf[kWaves][kSFlush * kTile];
 };
 
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
@@ -104,8 +107,27 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
     const float total = (lane < 32) ? sum + other : other + sum;
     const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
     if (lane < 32 && p < k1) {
-      srow[p] = total;
+      sm.sbuf[wave][(it % kSFlush) * kTile + lane] = total;
       atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
+    }
+    if ((it + 1) % kSFlush == 0 || it + 1 == ntw) {
+      // write the staged tiles in a burst: lane e stores 4 scores of tile first + e/8
+      // (16 bytes), so the writes interleave with the streaming reads as little as possible
+      wait_lgkm0();
+      const int first = (it / kSFlush) * kSFlush;
+      const int nt = it + 1 - first;
+      for (int e = lane; e < nt * 8; e += 64) {
+        const int tt = first + e / 8;
+        const int q0 = k0 + (wave + tt * kWaves) * kTile + (e % 8) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(&sm.sbuf[wave][(tt - first) * kTile + (e % 8) * 4]);
+        if (q0 + 3 < k1) {
+          *reinterpret_cast<float4*>(srow + q0) = v;
+        } else {
+          if (q0 < k1) srow[q0] = v.x;
+          if (q0 + 1 < k1) srow[q0 + 1] = v.y;
+          if (q0 + 2 < k1) srow[q0 + 2] = v.z;
+        }
+      }
     }
   }
   __syncthreads();
