@@ -216,6 +216,46 @@ def test_repeat_runs_are_bitwise_identical():
     assert np.array_equal(a["sparse"][0], b["sparse"][0])
 
 
+def test_sparse_split_merge_and_stage_reuse():
+    """100 single-query sequences: each query's 1,152 keys are split over three
+    workgroups of 15 tiles (every wave cycles through its LDS stages several times) and
+    the split combine merges the partials."""
+    lens = [2000 + 37 * j for j in range(100)]
+    spec = BlockSpec("split-merge", lens, [[n - 1] for n in lens], dtype="bf16", n_sparse=1, needles_per_query=1,
+                     seed=23)
+    inp = make_block_inputs(spec)
+    _say("sparse split merge")
+    g = run_block(inp)
+    check_queries(inp, g, range(0, spec.total_q, 7), "split-merge")
+    check_all_queries_properties(inp, g)
+
+
+def test_sparse_workspace_contents_do_not_matter():
+    """The sparse call's workspace (the split partials) holds arbitrary bytes on entry
+    and is used again and again: every call gives the same output."""
+    lens = [3000 + 101 * j for j in range(8)]
+    spec = BlockSpec("ws", lens, [[n - 1] for n in lens], dtype="bf16", n_sparse=1, needles_per_query=2, seed=24)
+    inp = make_block_inputs(spec)
+    g = run_block(inp)
+    q = to_dev(inp.q_sp[0])
+    sel = torch.from_numpy(g["sel"]).cuda()
+    need = hs2.sparse_attn_workspace_size(g["batch"], spec.window, spec.top_k)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill in (0xFF, 0x00, 0x01, None, None):
+        if fill is not None:
+            ws.fill_(fill)
+        o, _ = hs2.sparse_attn(g["batch"], q, g["k"], g["v"], sel, spec.window, spec.top_k, spec.scale, workspace=ws)
+        outs.append(from_dev(o))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o, g["sparse"][0])
+    for qi in range(spec.total_q):
+        r = oracle_query(inp, qi)
+        ref, _ = oracle_sparse(inp, qi, 0, g["sel"][qi], r["K"], r["V"])
+        check_attn(outs[-1][qi], ref, f"ws q{qi}")
+
+
 BRIDGE_ATOL = 2.0 ** -14
 
 
