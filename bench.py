@@ -6,7 +6,8 @@ the full-attention selector (exact causal MQA attention, head-summed scores, top
 selection) followed by every sparse layer of the hybrid block on the selector's KV and
 indices. The default workload is batched decode: 64 sequences x 131,072 cached tokens,
 one query each, 1 selector + 7 sparse layers (bf16). `--workload 3/4/5` measures the
-other workloads (5 also runs the KV Bridging projection of 1,048,576 hidden states).
+other workloads (5 also runs the KV Bridging projection of 1,048,576 hidden states);
+`--workload 6` is the default workload on an FP8 E4M3 K/V cache.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events recorded by the
 library around each kernel it launches, on the stream it launches on.
@@ -27,7 +28,6 @@ if ROOT not in sys.path:
 METRIC = "sparse-decode tokens/s & HBM GB/s at 128k/1M ctx; select+attn TFLOP/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-KV_ROW_BYTES = 2 * 128 * 2          # one K row + one V row, bf16
 QO_BYTES = 2 * 64 * 128 * 2         # one query's Q and O, bf16
 QK_PV_FLOPS = 2 * 2 * 64 * 128      # per (query, key): QK^T and PV over 64 heads
 SCORE_FLOPS = 2 * 64 * 128          # per candidate: the score pass recomputes QK^T
@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -87,11 +87,14 @@ def cpu_baseline(inp, budget_s: float):
     rng = np.random.default_rng(0)
     rng.shuffle(order)
     done, spent = 0, 0.0
+    def kv(rows, scale):
+        return oracle.dequantize_kv(rows, scale) if rows.dtype == np.uint8 else stored_to_f64(rows)
+
     for qi in order:
         s = int(inp.q_seq[qi])
         a, t = int(inp.kv_start[s]), int(inp.q_pos[qi])
-        K = stored_to_f64(inp.k[a:a + t + 1])
-        V = stored_to_f64(inp.v[a:a + t + 1])
+        K = kv(inp.k[a:a + t + 1], sp.k_scale)
+        V = kv(inp.v[a:a + t + 1], sp.v_scale)
         q = stored_to_f64(inp.q_sel[qi])
         qs = [stored_to_f64(x[qi]) for x in inp.q_sp]
         t0 = time.perf_counter()
@@ -153,10 +156,29 @@ def main() -> int:
     lse = torch.empty(nq, 64, dtype=torch.float32, device=dev)
     sel = torch.empty(nq, spec.top_k, dtype=torch.int32, device=dev)
     cnt = torch.empty(nq, dtype=torch.int32, device=dev)
-    ws_sel = torch.empty(hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k), dtype=torch.uint8,
-                         device=dev)
-    ws_sp = torch.empty(max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k)), dtype=torch.uint8,
-                        device=dev)
+    fp8 = spec.dtype == "fp8"
+    ws_dt = "fp8" if fp8 else torch.bfloat16
+    kv_row_bytes = 2 * 128 * (1 if fp8 else 2)  # one K row + one V row
+    ws_sel = torch.empty(hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k, ws_dt),
+                         dtype=torch.uint8, device=dev)
+    ws_sp = torch.empty(max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k, ws_dt)),
+                        dtype=torch.uint8, device=dev)
+
+    def select_call():
+        if fp8:
+            hs2.full_attn_select_fp8kv(batch, q_sel, k, v, spec.k_scale, spec.v_scale, spec.window, spec.top_k,
+                                       spec.scale, out=out, lse=lse, sel_idx=sel, sel_count=cnt, workspace=ws_sel)
+        else:
+            hs2.full_attn_select(batch, q_sel, k, v, spec.window, spec.top_k, spec.scale, out=out, lse=lse,
+                                 sel_idx=sel, sel_count=cnt, workspace=ws_sel)
+
+    def sparse_call(l):
+        if fp8:
+            hs2.sparse_attn_fp8kv(batch, q_sp[l], k, v, spec.k_scale, spec.v_scale, sel, spec.window, spec.top_k,
+                                  spec.scale, out=outs[l], workspace=ws_sp)
+        else:
+            hs2.sparse_attn(batch, q_sp[l], k, v, sel, spec.window, spec.top_k, spec.scale, out=outs[l],
+                            workspace=ws_sp)
     outs = [torch.empty_like(q_sel) for _ in range(spec.n_sparse)]
     bridge = None
     if args.workload == 5:
@@ -189,12 +211,10 @@ def main() -> int:
             attach(ev_br)
             hs2.bridge_kv(bridge["h"], bridge["wk"], bridge["wv"], bridge["ko"], bridge["vo"], workspace=bridge["ws"])
         attach(ev_sel)
-        hs2.full_attn_select(batch, q_sel, k, v, spec.window, spec.top_k, spec.scale, out=out, lse=lse,
-                             sel_idx=sel, sel_count=cnt, workspace=ws_sel)
+        select_call()
         for l in range(spec.n_sparse):
             attach(ev_sp[l] if ev_sp else None)
-            hs2.sparse_attn(batch, q_sp[l], k, v, sel, spec.window, spec.top_k, spec.scale, out=outs[l],
-                            workspace=ws_sp)
+            sparse_call(l)
         hs2.set_kernel_events(None)
 
     log(f"warmup {args.warmup}")
@@ -221,12 +241,10 @@ def main() -> int:
             hs2.set_kernel_events(None)
         else:
             hs2.set_kernel_events([e.cuda_event for e in evs])      # slot 0: pass 1
-        hs2.full_attn_select(batch, q_sel, k, v, spec.window, spec.top_k, spec.scale, out=out, lse=lse,
-                             sel_idx=sel, sel_count=cnt, workspace=ws_sel)
+        select_call()
         hs2.set_kernel_events(None)
         for l in range(spec.n_sparse):
-            hs2.sparse_attn(batch, q_sp[l], k, v, sel, spec.window, spec.top_k, spec.scale, out=outs[l],
-                            workspace=ws_sp)
+            sparse_call(l)
 
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
@@ -271,9 +289,9 @@ def main() -> int:
     keys = int(sum(int(t) + 1 for t in inp.q_pos))
     cands = int(sum(max(0, int(t) - spec.window + 1) for t in inp.q_pos))
     attended = int(sum(min(int(t) + 1, spec.window + spec.top_k) for t in inp.q_pos))
-    sel_bytes = keys * KV_ROW_BYTES if nq == spec.total_q and all(len(p) == 1 for p in spec.q_positions) \
-        else spec.total_rows * KV_ROW_BYTES
-    sparse_bytes = spec.n_sparse * (attended * KV_ROW_BYTES + nq * QO_BYTES)
+    sel_bytes = keys * kv_row_bytes if nq == spec.total_q and all(len(p) == 1 for p in spec.q_positions) \
+        else spec.total_rows * kv_row_bytes
+    sparse_bytes = spec.n_sparse * (attended * kv_row_bytes + nq * QO_BYTES)
     step_bytes = sel_bytes + sparse_bytes
     flops_attn = keys * QK_PV_FLOPS + spec.n_sparse * attended * QK_PV_FLOPS
     flops_score = cands * SCORE_FLOPS
@@ -290,7 +308,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) Q/K/V (bf16) with planted needle keys",
+        "data": ("synthetic: seeded N(0,1) Q (bf16), K/V as OCP FP8 E4M3 codes with per-tensor scales, planted "
+                 "needle keys" if fp8 else "synthetic: seeded N(0,1) Q/K/V (bf16) with planted needle keys"),
         "config": {"workload": spec.name, "seqs": len(spec.seq_lens), "queries": nq,
                    "ctx": int(max(spec.seq_lens)), "sparse_layers": spec.n_sparse, "window": spec.window,
                    "top_k": spec.top_k, "q_heads": 64, "kv_heads": 1, "head_dim": 128,
@@ -298,6 +317,9 @@ def main() -> int:
     }
     if args.workload == 5:
         res["config"]["bridging"] = {"rows": 1048576, "d_model": 2048, "layers": 3}
+    if fp8:
+        res["config"]["kv_storage"] = {"format": "OCP FP8 E4M3", "k_scale": spec.k_scale, "v_scale": spec.v_scale,
+                                       "compute": "codes converted exactly to bf16 for the MFMA"}
     if bridge is not None:
         f = 2 * 1048576 * 2048 * 256 * 3
         ach = f / (roof_ms * 1e-3) / 1e12
@@ -306,7 +328,7 @@ def main() -> int:
                            "frac": ach / BF16_PEAK_TFLOPS, "traffic": None, "alg_flops_per_launch": f,
                            "avg_launch_ms": roof_ms}
     elif decode:
-        a_bytes = keys * KV_ROW_BYTES
+        a_bytes = keys * kv_row_bytes
         res["roofline"] = {"kernel": "attn_pass1 (selector exact attention, K+V once)", "bound": "hbm",
                            "achieved": a_bytes / (roof_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                            "unit": "GB/s", "frac": a_bytes / (roof_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -327,7 +349,7 @@ def main() -> int:
     }
     res["kernels_ms"] = kern
     res["kernels_ms_source"] = f"HIP events around every kernel over {n_prof} steps after the timed ones"
-    res["sparse_layer_gbps_alg"] = (attended * KV_ROW_BYTES + nq * QO_BYTES) / (
+    res["sparse_layer_gbps_alg"] = (attended * kv_row_bytes + nq * QO_BYTES) / (
         sparse_layer_ms * 1e-3) / 1e9 if spec.n_sparse else None
     if bridge is not None:
         bf = 2 * 1048576 * 2048 * 256 * 3

@@ -71,8 +71,11 @@ typedef enum hs2_status {
 } hs2_status;
 
 typedef enum hs2_dtype {
-  HS2_BF16 = 0, /* bfloat16 storage, fp32 arithmetic (bf16 MFMA with fp32 accumulation) */
-  HS2_F32 = 1   /* float32 storage and arithmetic                                      */
+  HS2_BF16 = 0,    /* bfloat16 storage, fp32 arithmetic (bf16 MFMA with fp32 accumulation) */
+  HS2_F32 = 1,     /* float32 storage and arithmetic                                      */
+  HS2_FP8_E4M3 = 2 /* K and V stored as OCP FP8 E4M3 codes with one scale per tensor; Q and
+                      out bfloat16. Taken by the *_fp8kv entry points and the workspace
+                      size queries (the other entry points return HS2_ERR_UNSUPPORTED)  */
 } hs2_dtype;
 
 /* A ragged batch of sequences and their queries. */
@@ -178,6 +181,37 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
                            const int32_t* sel_idx, int32_t n_heads, int32_t head_dim,
                            int32_t window, int32_t top_k, float scale, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * FP8 KV cache ([arex] "Numbers computed on three 80B-A3B models": the pages' KV-cache
+ * accounting at 1M tokens stores K and V in FP8). The same two operations as
+ * hs2_full_attn_select and hs2_sparse_attn, on a cache whose rows are OCP FP8 E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals; 0x7F and
+ * 0xFF are NaN; no infinities; largest finite 448). Row j of the cache stands for
+ *     k_j = k_scale * decode(k[j][:]),   v_j = v_scale * decode(v[j][:])
+ * and every result is that of the bf16 operation on those values: the codes convert to
+ * bf16 exactly, K's scale multiplies the logit scale and V's the output, in fp32.
+ *
+ *   k, v      device [total_kv_rows][128] uint8 (E4M3 codes), 16-byte aligned
+ *   k_scale,  per-tensor scales, finite and > 0
+ *   v_scale
+ *   q, out    bf16 as in the bf16 operations; other arguments as there. Workspace sizes
+ *             come from the size queries with dt = HS2_FP8_E4M3. The selector always
+ *             uses its one-query-per-workgroup kernels (no q-tile path for FP8).
+ * ------------------------------------------------------------------------------------ */
+hs2_status hs2_full_attn_select_fp8kv(const hs2_seqs* batch, const void* q, const void* k,
+                                      const void* v, float k_scale, float v_scale,
+                                      int32_t n_heads, int32_t head_dim, int32_t window,
+                                      int32_t top_k, float scale, void* out, float* lse,
+                                      int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+hs2_status hs2_sparse_attn_fp8kv(const hs2_seqs* batch, const void* q, const void* k,
+                                 const void* v, float k_scale, float v_scale,
+                                 const int32_t* sel_idx, int32_t n_heads, int32_t head_dim,
+                                 int32_t window, int32_t top_k, float scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Kernel timing hook, for benchmarks and profilers that need per-kernel durations on the

@@ -42,9 +42,13 @@ using namespace attn;
 constexpr int kSelMax = 2048;  // gathered slots per workgroup (the host caps the split)
 constexpr int kSelPerThread = kSelMax / 256;
 
+constexpr int kWaveStageBytes = 32768;  // per wave: Kv::kStages x (K + V) tiles
+static_assert(KvBf16::kStages * 2 * KvBf16::kTileBytes == kWaveStageBytes, "bf16 stages");
+static_assert(KvFp8::kStages * 2 * KvFp8::kTileBytes == kWaveStageBytes, "fp8 stages");
+
 struct AttnSmem {
   union {
-    uint8_t stage[kWaves][kStages][2][kTileBytes];
+    uint8_t stage[kWaves][kWaveStageBytes];  // stage j of a wave: K tile at 2j, V tile at 2j+1
     struct {
       float m[kWaves][kHeads];
       float l[kWaves][kHeads];
@@ -61,54 +65,70 @@ struct AttnSmem {
 };
 
 // Streams the tiles wave, wave + 4, ... of the workgroup's key range through the wave's
-// two LDS stages. DMA groups are issued in the order K0 V0 K1 V1, then per iteration
-// K(it+2) right after the K operands of tile it are in registers and V(it+2) after its
-// PV step, so two tiles stream in while one is computed. Waits count the 8-load groups
-// issued later. kMaxOnly: only the logit maximum of the attended keys (into mx).
-template <bool kMaxOnly>
-__device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem& sm, const KeyList& kl, int k0, int k1,
-                                    int ntiles, const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
-                                    float c2, int wave, int lane) {
-  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  uint32_t lk[kStages], lv[kStages];
-#pragma unroll
-  for (int sidx = 0; sidx < kStages; ++sidx) {
-    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][0]);
-    lv[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx][1]);
+// S = Kv::kStages LDS stages. DMA groups are issued in the order K0 V0 K1 V1 ..., then per
+// tile K(it+S) right after the K operands of tile it are in registers and V(it+S) after
+// its PV step, so S tiles stream in while one is computed. Waits count the copies issued
+// later: constant in the steady state, and in the last S tiles a compile-time count per
+// tile (the tail is unrolled), so the loop has no branches around its waits. The mask of
+// attended keys is recomputed when a tile is processed (no per-stage state). kMaxOnly:
+// only the logit maximum of the attended keys (into mx).
+template <typename Kv, bool kMaxOnly, int kLater, bool kMore>
+__device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem& sm, const KeyList& kl, int k0, int k1,
+                                   const void* __restrict__ kp, const void* __restrict__ vp, float c2, int wave,
+                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, int it) {
+  constexpr int S = Kv::kStages, D = Kv::kDma, T = Kv::kTileBytes;
+  const int sidx = it % S;
+  wait_vmcnt<D * (1 + 2 * kLater)>();  // K(it) has landed
+  const uint8_t* kt = sm.stage[wave] + (2 * sidx) * T;
+  bf16x8 kop[8];
+  read_k_of<Kv>(kt, lane, kop);
+  int rel;
+  const uint32_t vm = tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, rel);
+  if (kMore) {
+    tile_rows(kl, k0 + (wave + (it + S) * kWaves) * kTile, k1, lane, rel);
+    issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * sidx) * T);
   }
-  uint32_t vb[4];
-  vt_bases(lane, vb);
-  uint32_t okm[kStages] = {0u, 0u};
-  int relv[kStages] = {0, 0};
-  for (int it = 0; it < min(ntw, kStages); ++it) {
-    okm[it] = tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, relv[it]);
-    issue_rows<true>(kp, kl.base, relv[it], lane, lk[it]);
-    issue_rows<false>(vp, kl.base, relv[it], lane, lv[it]);
+  wait_vmcnt<D * (2 * kLater + (kMore ? 1 : 0))>();  // V(it) has landed
+  if (vm != 0u) {
+    if (kMaxOnly)
+      process_tile_max<false>(mx, sm.q, nullptr, kop, vm, c2, lane);
+    else
+      process_tile<false, Kv>(st, sm.q, nullptr, kop, kt + T, vb, vm, c2, lane);
   }
-  for (int it = 0; it < ntw; ++it) {
-    const int sidx = it & 1;
-    const bool more1 = it + 1 < ntw, more2 = it + 2 < ntw;
-    wait_vmcnt_dyn(more1 ? 24 : 8);  // K(it) has landed
-    bf16x8 kop[8];
-    read_k(sm.stage[wave][sidx][0], lane, kop);
-    const uint32_t vm = okm[sidx];
-    int rel2 = 0;
-    if (more2) {
-      okm[sidx] = tile_rows(kl, k0 + (wave + (it + 2) * kWaves) * kTile, k1, lane, rel2);
-      issue_rows<true>(kp, kl.base, rel2, lane, lk[sidx]);
-    }
-    wait_vmcnt_dyn((more1 ? 16 : 0) + (more2 ? 8 : 0));  // V(it) has landed
-    if (vm != 0u) {
-      if (kMaxOnly)
-        process_tile_max<false>(mx, sm.q, nullptr, kop, vm, c2, lane);
-      else
-        process_tile<false>(st, sm.q, nullptr, kop, sm.stage[wave][sidx][1], vb, vm, c2, lane);
-    }
-    if (more2) issue_rows<false>(vp, kl.base, rel2, lane, lv[sidx]);
-  }
+  if (kMore) issue_tile<Kv, false>(vp, kl.base, rel, lane, wbase + (2 * sidx + 1) * T);
 }
 
-template <bool kGather>
+template <typename Kv, bool kMaxOnly, int kLater>
+__device__ inline void stream_tail(WaveState& st, float (&mx)[2], AttnSmem& sm, const KeyList& kl, int k0, int k1,
+                                   const void* __restrict__ kp, const void* __restrict__ vp, float c2, int wave,
+                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, int ntw) {
+  const int it = ntw - 1 - kLater;
+  if (it >= 0) stream_step<Kv, kMaxOnly, kLater, false>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, it);
+  if constexpr (kLater > 0)
+    stream_tail<Kv, kMaxOnly, kLater - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ntw);
+}
+
+template <typename Kv, bool kMaxOnly>
+__device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem& sm, const KeyList& kl, int k0, int k1,
+                                    int ntiles, const void* __restrict__ kp, const void* __restrict__ vp,
+                                    float c2, int wave, int lane) {
+  constexpr int S = Kv::kStages, T = Kv::kTileBytes;
+  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
+  uint32_t vb[4];
+  vt_bases_of<Kv>(lane, vb);
+  for (int it = 0; it < min(ntw, S); ++it) {
+    int rel;
+    tile_rows(kl, k0 + (wave + it * kWaves) * kTile, k1, lane, rel);
+    issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * it) * T);
+    issue_tile<Kv, false>(vp, kl.base, rel, lane, wbase + (2 * it + 1) * T);
+  }
+  for (int it = 0; it + S < ntw; ++it)
+    stream_step<Kv, kMaxOnly, S - 1, true>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, it);
+  stream_tail<Kv, kMaxOnly, S - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ntw);
+}
+
+template <typename Kv, bool kGather>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, WorkList wl, uint32_t* hist,
                                                         uint32_t* counters) {
   __shared__ __align__(16) AttnSmem sm;
@@ -144,7 +164,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, WorkList wl,
 
   int64_t base;
   int t;
-  const bool valid = query_desc(a.b, i, base, t);
+  const bool valid = __builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t));
+  // the descriptor is the same on every lane (query i): keep the loop control scalar
+  t = __builtin_amdgcn_readfirstlane(t);
+  base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
+                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
   if (a.n_split == 1 && hist != nullptr) {
     for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) hist[(size_t)i * kHistBins + e] = 0u;
     if (threadIdx.x < 4) counters[(size_t)i * 4 + threadIdx.x] = 0u;
@@ -185,21 +209,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, WorkList wl,
   for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8*>(sm.q + ((int)threadIdx.x + 256 * u) * 16) = qv[u];
   __syncthreads();
 
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* vp = static_cast<const __bf16*>(a.v);
+  const void* kp = a.k;
+  const void* vp = a.v;
   WaveState st;
   state_init(st);
   float mx[2] = {-INFINITY, -INFINITY};
-  stream_tiles<false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+  stream_tiles<Kv, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
   if (!state_finite(st)) {
     // rare: a logit far above the first tile's maximum overflowed the sums; recompute
     // with the exact maximum of this wave's keys as reference (every weight <= 1)
-    stream_tiles<true>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+    stream_tiles<Kv, true>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
     state_init(st);
     st.m[0] = mx[0];
     st.m[1] = mx[1];
     st.have_ref = 1;
-    stream_tiles<false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+    stream_tiles<Kv, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
   }
 
 #pragma unroll
@@ -264,7 +288,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, WorkList wl,
   const int h = threadIdx.x & 63, dq = threadIdx.x >> 6;
   if (a.n_split == 1) {
     __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)i * kHeads + h) * kDim + 32 * dq;
-    const float inv = 1.0f / sm.mg.fl[h];
+    const float inv = a.v_scale / sm.mg.fl[h];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8 v;
@@ -388,7 +412,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] += P[s2].o[(d0 + r) * kHeads + h] * w;
   }
-  const float inv = 1.0f / fl[h];
+  const float inv = a.v_scale / fl[h];
 #pragma unroll
   for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)(acc[r] * inv);
 }
@@ -398,9 +422,18 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
                             uint32_t* counters, hipStream_t s) {
   if (gather)
-    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+    hipLaunchKernelGGL((attn_bf16_kernel<KvBf16, true>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+    hipLaunchKernelGGL((attn_bf16_kernel<KvBf16, false>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
+                             uint32_t* counters, hipStream_t s) {
+  if (gather)
+    hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, true>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, false>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
   return hipGetLastError();
 }
 

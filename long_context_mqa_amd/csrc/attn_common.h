@@ -12,9 +12,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kNegBig = -1.0e30f; // "no key yet" reference
-constexpr int kTileBytes = kTile * kDim * 2;  // 8 KB: one K or V tile
+constexpr int kTileBytes = kTile * kDim * 2;  // 8 KB: one bf16 K or V tile
 constexpr int kStages = 2;                    // per-wave LDS stages (K + V each)
 constexpr int kDmaPerHalf = kTileBytes / 1024;     // 8 wave-wide 16-byte loads per K or V tile
+
+// Storage formats of the K and V rows. The MFMA operands are bf16 in both: an OCP FP8
+// E4M3 value converts to bf16 exactly (3 mantissa bits, exponents 2^-9 .. 2^8), and the
+// per-tensor scales are applied in fp32 outside the products (the K scale in the logit
+// scale, the V scale in the output normalisation).
+struct KvBf16 {
+  static constexpr bool kFp8 = false;
+  static constexpr int kRowBytes = kDim * 2;              // 256
+  static constexpr int kTileBytes = kTile * kRowBytes;    // 8 KB
+  static constexpr int kDma = kTileBytes / 1024;          // wave-wide 16-byte copies per tile
+  static constexpr int kStages = 2;                       // pass-1 stages per wave (K + V)
+};
+struct KvFp8 {
+  static constexpr bool kFp8 = true;
+  static constexpr int kRowBytes = kDim;                  // 128
+  static constexpr int kTileBytes = kTile * kRowBytes;    // 4 KB
+  static constexpr int kDma = kTileBytes / 1024;
+  static constexpr int kStages = 4;                       // same bytes in flight as bf16
+};
 
 __device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -39,6 +58,15 @@ __device__ inline uint32_t tile_off(int row, int chunk) {
   return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4));
 }
 __device__ inline int v_chunk(int row, int pos) { return pos ^ ((row & 3) << 2); }
+
+// FP8 tiles (32 rows of 128 bytes = 8 chunks of 16):
+//  K: chunk c of row r at position c ^ ((r >> 1) & 7): the operand reads (16 rows, same
+//     chunk, per 256 bytes of LDS) cover all 16 bank groups;
+//  V: chunk c of row r at position c ^ ((r & 2) | ((r >> 1) & 4)): the transposing reads
+//     take 8 rows x 2 adjacent chunks (rows {0,1,2,3,8,9,10,11} + 4h of a 16-key step),
+//     which this maps onto 16 distinct bank groups.
+__device__ inline int k8_swz(int row) { return (row >> 1) & 7; }
+__device__ inline int v8_swz(int row) { return (row & 2) | ((row >> 1) & 4); }
 
 // Logical key list of one query. Full mode: positions 0..t. Gather mode: top_k selected
 // slots (entries outside the candidate range are masked) followed by the window rows.
@@ -88,6 +116,25 @@ __device__ inline void issue_rows(const __bf16* __restrict__ src, int64_t base, 
     const int row = r * 4 + (lane >> 4);
     const int chunk = kIsK ? ((lane & 15) ^ (row & 15)) : v_chunk(row, lane & 15);
     dma16(src + (base + __shfl(rel, row)) * kDim + chunk * 8, lds + r * 1024);
+  }
+}
+
+// The same for either storage format (src: the K or V tensor): copy r writes the
+// 1024/kRowBytes rows that follow row r*1024/kRowBytes, each lane one 16-byte position.
+template <typename Kv, bool kIsK>
+__device__ inline void issue_tile(const void* __restrict__ src, int64_t base, int rel, int lane, uint32_t lds) {
+  if constexpr (!Kv::kFp8) {
+    issue_rows<kIsK>(static_cast<const __bf16*>(src), base, rel, lane, lds);
+  } else {
+    wait_lgkm0();
+    const uint8_t* s8 = static_cast<const uint8_t*>(src);
+#pragma unroll
+    for (int r = 0; r < Kv::kDma; ++r) {
+      const int row = r * 8 + (lane >> 3);
+      const int pos = lane & 7;
+      const int chunk = pos ^ (kIsK ? k8_swz(row) : v8_swz(row));
+      dma16(s8 + (base + __shfl(rel, row)) * Kv::kRowBytes + chunk * 16, lds + r * 1024);
+    }
   }
 }
 
@@ -148,6 +195,45 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// FP8 V^T operands (ds_read_b64_tr_b8). In each 16-lane group g, output lane j receives
+// as its byte c the byte j%8 of the 8 bytes addressed by lane 2c + j/8 of the group
+// (lane mapping established with an in-bounds probe on the GPU). Lane 2c + h of group g
+// addresses row key(c) = 16ks + 8(c/4) + 4(g/2) + c%4 at dims 32mb + 16(g%2) + 8h, so
+// output lane l holds V[key(c)][32mb + l%32] for c = 0..7: the A operand of
+// O^T += V^T P^T in the key order of the P^T operand (see process_tile).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ inline void vt8_bases(int lane, uint32_t (&vb)[4]) {
+  const int g = lane >> 4, c = (lane & 15) >> 1, h = lane & 1;
+  const int row = 8 * (c >> 2) + 4 * (g >> 1) + (c & 3);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+    vb[mb] = (uint32_t)(row * 128 + (((2 * mb + (g & 1)) ^ v8_swz(row)) << 4) + 8 * h);
+}
+
+template <typename Kv>
+__device__ inline void vt_bases_of(int lane, uint32_t (&vb)[4]) {
+  if constexpr (Kv::kFp8) vt8_bases(lane, vb);
+  else vt_bases(lane, vb);
+}
+
+// Eight OCP E4M3 codes (bytes of w0, then w1) to bf16, exactly (scale 1).
+__device__ inline bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ inline bf16x8 read_vt8(const uint8_t* vt, uint32_t vbase, int ks) {
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(vt) + vbase + ks * 16 * 128;
+  const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+  return fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+}
+
 __device__ inline bf16x8 read_vt(const uint8_t* vt, uint32_t vbase, int ks) {
   const __attribute__((address_space(3))) char* p =
       (const __attribute__((address_space(3))) char*)(vt) + vbase + ks * 16 * 256;
@@ -191,7 +277,7 @@ __device__ inline void tile_max(const f32x16 (&acc)[2], uint32_t vm, float c2, i
 // One 32-key tile with at least one attended key: S^T = K Q^T, P = exp2(c2 S - m) with
 // the fixed reference, O^T += V^T P^T. Q^T operands come from LDS or registers, K
 // operands were read already, V^T is read from the tile's stage in LDS.
-template <bool kQReg>
+template <bool kQReg, typename Kv = KvBf16>
 __device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ qs, const bf16x8 (*qreg)[8],
                                     const bf16x8 (&kop)[8], const uint8_t* __restrict__ vt, const uint32_t (&vb)[4],
                                     uint32_t vm, float c2, int lane) {
@@ -247,7 +333,9 @@ __device__ inline void process_tile(WaveState& st, const uint8_t* __restrict__ q
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 va = read_vt(vt, vb[mb], ks);
+      bf16x8 va;
+      if constexpr (Kv::kFp8) va = read_vt8(vt, vb[mb], ks);
+      else va = read_vt(vt, vb[mb], ks);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) st.o[nb][mb] = mfma(va, pb[nb][ks], st.o[nb][mb]);
     }
@@ -271,6 +359,49 @@ __device__ inline void read_k(const uint8_t* __restrict__ kt, int lane, bf16x8 (
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     kop[s] = *reinterpret_cast<const bf16x8*>(kt + tile_off(row, (lane >> 5) * 8 + s));
+}
+
+// K A-operands from an FP8 K tile: lane l reads the 64 bytes of dims (l/32)*64 .. +63 of
+// row l%32 (4 chunks; each holds the 8-dim slices of two contraction steps) and
+// converts them to bf16.
+__device__ inline void read_k8(const uint8_t* __restrict__ kt, int lane, bf16x8 (&kop)[8]) {
+  const int row = lane & 31;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int chunk = 4 * (lane >> 5) + u;
+    const uint4 w = *reinterpret_cast<const uint4*>(kt + row * 128 + ((chunk ^ k8_swz(row)) << 4));
+    kop[2 * u] = fp8x8_to_bf16(w.x, w.y);
+    kop[2 * u + 1] = fp8x8_to_bf16(w.z, w.w);
+  }
+}
+
+template <typename Kv>
+__device__ inline void read_k_of(const uint8_t* __restrict__ kt, int lane, bf16x8 (&kop)[8]) {
+  if constexpr (Kv::kFp8) read_k8(kt, lane, kop);
+  else read_k(kt, lane, kop);
+}
+
+// s_waitcnt vmcnt(n) for a run-time, wave-uniform n, a multiple of 4 below 64
+__device__ inline void wait_vmcnt_n(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 28: wait_vmcnt<28>(); break;
+    case 32: wait_vmcnt<32>(); break;
+    case 36: wait_vmcnt<36>(); break;
+    case 40: wait_vmcnt<40>(); break;
+    case 44: wait_vmcnt<44>(); break;
+    case 48: wait_vmcnt<48>(); break;
+    case 52: wait_vmcnt<52>(); break;
+    case 56: wait_vmcnt<56>(); break;
+    case 60: wait_vmcnt<60>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
 }
 
 // s_waitcnt vmcnt(n) for a run-time n in {0, 8, 16, 24}

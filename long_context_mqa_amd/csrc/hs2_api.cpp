@@ -150,7 +150,7 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
     p.attn = split_of(b->max_kv_len, std::numeric_limits<int>::max());
     p.score = split_of(max_cand, kScoreSplitMax);
   } else {
-    const bool lists = dt == HS2_BF16;
+    const bool lists = dt != HS2_F32;  // the bf16 and FP8 decode-shaped kernels take work lists
     if (!plan_split_lengths(b, 0, b->max_kv_len, p.attn, lists ? &p.attn_wl : nullptr))
       p.attn = plan_split(launch_work(b, b->max_kv_len), b->max_kv_len);
     if (!plan_split_lengths(b, window - 1, max_cand, p.score, lists ? &p.score_wl : nullptr))
@@ -221,7 +221,8 @@ hs2_status check_attn_common(const hs2_seqs* b, const void* q, const void* k, co
                              float scale, const void* out, const float* lse, hs2_dtype dt) {
   hs2_status st = check_batch(b);
   if (st != HS2_OK) return st;
-  if (dt != HS2_BF16 && dt != HS2_F32) return fail(HS2_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dt);
+  if (dt != HS2_BF16 && dt != HS2_F32 && dt != HS2_FP8_E4M3)
+    return fail(HS2_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dt);
   if (n_heads != kHeads || head_dim != kDim)
     return fail(HS2_ERR_UNSUPPORTED, "only n_heads=64, head_dim=128 are supported (got %d, %d)", n_heads,
                 head_dim);
@@ -306,11 +307,28 @@ size_t hs2_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_head
   return plan_select(batch, window, top_k, dt).total;
 }
 
-hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
-                                int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,
-                                float scale, void* out, float* lse, int32_t* sel_idx,
-                                int32_t* sel_count, void* workspace, size_t workspace_bytes,
-                                hs2_dtype dt, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// FP8 K/V: the per-tensor scales must be finite and positive.
+hs2_status check_kv_scales(float k_scale, float v_scale) {
+  if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) || !std::isfinite(v_scale))
+    return fail(HS2_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  return HS2_OK;
+}
+
+// Softmax constant of the kernels: scale * log2(e), times the K scale of FP8 storage
+// (logit = scale * <q, k_scale * code> = (scale * k_scale) * <q, code>).
+float logit_c2(float scale, hs2_dtype dt, float k_scale) {
+  if (dt != HS2_FP8_E4M3) return scale * kLog2e;
+  return (float)((double)scale * (double)k_scale * 1.4426950408889634);
+}
+
+hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, const void* v, float k_scale,
+                       float v_scale, int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,
+                       float scale, void* out, float* lse, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                       size_t workspace_bytes, hs2_dtype dt, void* stream) {
   hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, window, top_k, scale, out, lse, dt);
   if (st != HS2_OK) return st;
   if (top_k > 0 && batch->total_q > 0 && !sel_idx)
@@ -326,6 +344,7 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f32 = dt == HS2_F32;
+  const bool fp8 = dt == HS2_FP8_E4M3;
   const int tq = batch->total_q;
   float* lse2 = at<float>(workspace, p.off_lse2);
   uint32_t* hist = at<uint32_t>(workspace, p.off_hist);
@@ -339,13 +358,14 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
   a.sel = nullptr;
   a.window = window;
   a.top_k = top_k;
-  a.c2 = scale * kLog2e;
+  a.c2 = logit_c2(scale, dt, k_scale);
   a.n_split = p.attn.n_split;
   a.split_keys = p.attn.split_keys;
   a.part = p.attn.n_split > 1 ? at<Partial>(workspace, p.off_part) : nullptr;
   a.out = out;
   a.lse = lse;
   a.lse2 = lse2;
+  a.v_scale = fp8 ? v_scale : 1.0f;
   const int grid = tq * p.attn.n_split;
   int2* tiles = p.chunk ? at<int2>(workspace, p.off_tiles) : nullptr;
   LaunchMarks mk(s);
@@ -359,9 +379,12 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
   if (e == hipSuccess) {
     if (p.chunk)
       e = launch_attn_chunk(a, tiles, p.max_tiles, s);
+    else if (f32)
+      e = launch_attn_f32(a, false, grid, hist, counters, s);
+    else if (fp8)
+      e = launch_attn_fp8kv(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
     else
-      e = f32 ? launch_attn_f32(a, false, grid, hist, counters, s)
-              : launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
+      e = launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
   }
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "full attention launch");
@@ -379,6 +402,7 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     c.lse2 = lse2;
     c.hist = hist;
     c.counters = counters;
+    c.v_scale = a.v_scale;
     e = mk.before(1);
     if (e == hipSuccess) e = launch_combine(c, f32, s);
     if (e == hipSuccess) e = mk.after(1);
@@ -416,8 +440,12 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
     if (e == hipSuccess) {
       if (p.chunk)
         e = launch_score_chunk(sc, tiles, p.max_tiles, s);
+      else if (f32)
+        e = launch_score_f32(sc, s);
+      else if (fp8)
+        e = launch_score_fp8kv(sc, p.score_wl, s);
       else
-        e = f32 ? launch_score_f32(sc, s) : launch_score_bf16(sc, p.score_wl, s);
+        e = launch_score_bf16(sc, p.score_wl, s);
     }
     if (e == hipSuccess) e = mk.after(2);
     if (e != hipSuccess) return hip_fail(e, "score launch");
@@ -433,19 +461,10 @@ hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void
   return ok();
 }
 
-size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim, int32_t window,
-                                      int32_t top_k, hs2_dtype dt) {
-  (void)n_heads;
-  (void)head_dim;
-  (void)dt;
-  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
-  return plan_sparse(batch, window, top_k).total;
-}
-
-hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
-                           const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
-                           int32_t top_k, float scale, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, hs2_dtype dt, void* stream) {
+hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, const void* v, float k_scale,
+                       float v_scale, const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
+                       int32_t top_k, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hs2_dtype dt, void* stream) {
   hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, window, top_k, scale, out, lse, dt);
   if (st != HS2_OK) return st;
   if (top_k > 0 && batch->total_q > 0 && !sel_idx)
@@ -460,6 +479,7 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f32 = dt == HS2_F32;
+  const bool fp8 = dt == HS2_FP8_E4M3;
   AttnArgs a{};
   a.b = to_dev(batch);
   a.q = q;
@@ -468,19 +488,21 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
   a.sel = sel_idx;
   a.window = window;
   a.top_k = top_k;
-  a.c2 = scale * kLog2e;
+  a.c2 = logit_c2(scale, dt, k_scale);
   a.n_split = p.attn.n_split;
   a.split_keys = p.attn.split_keys;
   a.part = p.attn.n_split > 1 ? static_cast<Partial*>(workspace) : nullptr;
   a.out = out;
   a.lse = lse;
   a.lse2 = nullptr;
+  a.v_scale = fp8 ? v_scale : 1.0f;
   const int grid = batch->total_q * p.attn.n_split;
   LaunchMarks mk(s);
   hipError_t e = mk.before(0);
   if (e == hipSuccess)
-    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
-            : launch_attn_bf16(a, WorkList{}, true, grid, nullptr, nullptr, s);
+    e = f32   ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
+        : fp8 ? launch_attn_fp8kv(a, WorkList{}, true, grid, nullptr, nullptr, s)
+              : launch_attn_bf16(a, WorkList{}, true, grid, nullptr, nullptr, s);
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   if (p.attn.n_split > 1) {
@@ -497,12 +519,68 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
     c.lse2 = nullptr;
     c.hist = nullptr;
     c.counters = nullptr;
+    c.v_scale = a.v_scale;
     e = mk.before(1);
     if (e == hipSuccess) e = launch_combine(c, f32, s);
     if (e == hipSuccess) e = mk.after(1);
     if (e != hipSuccess) return hip_fail(e, "split combine launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,
+                                float scale, void* out, float* lse, int32_t* sel_idx,
+                                int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                hs2_dtype dt, void* stream) {
+  if (dt == HS2_FP8_E4M3)
+    return fail(HS2_ERR_UNSUPPORTED, "FP8 K/V needs its scales: use hs2_full_attn_select_fp8kv");
+  return select_impl(batch, q, k, v, 1.0f, 1.0f, n_heads, head_dim, window, top_k, scale, out, lse, sel_idx,
+                     sel_count, workspace, workspace_bytes, dt, stream);
+}
+
+hs2_status hs2_full_attn_select_fp8kv(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                      float k_scale, float v_scale, int32_t n_heads, int32_t head_dim,
+                                      int32_t window, int32_t top_k, float scale, void* out, float* lse,
+                                      int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  hs2_status st = check_kv_scales(k_scale, v_scale);
+  if (st != HS2_OK) return st;
+  return select_impl(batch, q, k, v, k_scale, v_scale, n_heads, head_dim, window, top_k, scale, out, lse, sel_idx,
+                     sel_count, workspace, workspace_bytes, HS2_FP8_E4M3, stream);
+}
+
+hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                           const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
+                           int32_t top_k, float scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  if (dt == HS2_FP8_E4M3) return fail(HS2_ERR_UNSUPPORTED, "FP8 K/V needs its scales: use hs2_sparse_attn_fp8kv");
+  return sparse_impl(batch, q, k, v, 1.0f, 1.0f, sel_idx, n_heads, head_dim, window, top_k, scale, out, lse,
+                     workspace, workspace_bytes, dt, stream);
+}
+
+hs2_status hs2_sparse_attn_fp8kv(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                 float k_scale, float v_scale, const int32_t* sel_idx, int32_t n_heads,
+                                 int32_t head_dim, int32_t window, int32_t top_k, float scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  hs2_status st = check_kv_scales(k_scale, v_scale);
+  if (st != HS2_OK) return st;
+  return sparse_impl(batch, q, k, v, k_scale, v_scale, sel_idx, n_heads, head_dim, window, top_k, scale, out, lse,
+                     workspace, workspace_bytes, HS2_FP8_E4M3, stream);
+}
+
+
+size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim, int32_t window,
+                                      int32_t top_k, hs2_dtype dt) {
+  (void)n_heads;
+  (void)head_dim;
+  (void)dt;
+  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
+  return plan_sparse(batch, window, top_k).total;
 }
 
 size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t head_dim) {

@@ -61,6 +61,7 @@ struct AttnArgs {
   void* out;              // [total_q][64][128] when n_split == 1
   float* lse;             // [total_q][64] natural log, nullable (n_split == 1)
   float* lse2;            // [total_q][64] log2 domain, nullable (n_split == 1)
+  float v_scale;          // output factor (the V scale of FP8 storage; 1 otherwise)
 };
 
 // (query, split) pairs of a launch in launch order: workgroup b takes item b, so that the
@@ -96,6 +97,7 @@ struct CombineArgs {
   float* lse2;            // nullable
   uint32_t* hist;         // nullable: [total_q][kHistBins] zeroed here for the score pass
   uint32_t* counters;     // nullable: [total_q][4] zeroed here
+  float v_scale;          // output factor (the V scale of FP8 storage; 1 otherwise)
 };
 
 struct ScoreArgs {
@@ -192,6 +194,8 @@ __device__ inline int logical_keys(bool gather, int t, int window, int top_k) {
 // ---------------------------------------------------------------------------------
 hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
                             uint32_t* counters, hipStream_t s);
+hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
+                             uint32_t* counters, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
                            uint32_t* counters, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
@@ -199,6 +203,7 @@ hipError_t launch_qtile_prep(const SeqsDev& b, int2* tiles, int max_tiles, hipSt
 hipError_t launch_attn_chunk(const AttnArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_score_bf16(const ScoreArgs& a, const WorkList& wl, hipStream_t s);
+hipError_t launch_score_fp8kv(const ScoreArgs& a, const WorkList& wl, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s);

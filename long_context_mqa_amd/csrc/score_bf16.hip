@@ -19,19 +19,22 @@ using namespace attn;
 // written per query, plus a histogram of the first radix digit (bits 30..19).
 // S = Q K^T here (heads as rows): each lane sums its 32 head values of one key, and one
 // exchange with lane l^32 completes the 64-head sum. K tiles stream through kScoreStages
-// per-wave LDS stages (same swizzled layout and DMA as pass 1).
+// per-wave LDS stages (same swizzled layout and DMA as pass 1): 4 of bf16 tiles or 8 of
+// FP8 tiles, the same bytes in flight.
 // ------------------------------------------------------------------------------------
-constexpr int kScoreStages = 4;
+constexpr int kScoreWaveBytes = 32768;  // LDS stage bytes per wave
 
 constexpr int kSFlush = 32;  // tiles of scores staged per wave before they are written
 
 struct ScoreSmem {
-  uint8_t stage[kWaves][kScoreStages][kTileBytes];
+  uint8_t stage[kWaves][kScoreWaveBytes];
   uint32_t hist[kHistBins];
   float sbuf[kWaves][kSFlush * kTile];
 };
 
+template <typename Kv>
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
+  constexpr int kScoreStages = kScoreWaveBytes / Kv::kTileBytes;
   __shared__ __align__(16) ScoreSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -39,7 +42,11 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
   work_item(wl, a.n_split, i, split);
   int64_t base;
   int t;
-  if (!query_desc(a.b, i, base, t)) return;
+  if (!__builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t))) return;
+  // the descriptor is the same on every lane (query i): keep the loop control scalar
+  t = __builtin_amdgcn_readfirstlane(t);
+  base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
+                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
   const int nc = max(0, t - a.window + 1);
   if (nc <= a.top_k) return;
   const int k0 = split * a.split_keys;
@@ -68,28 +75,24 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
       l2[mb][j] = a.lse2[(size_t)i * kHeads + 32 * mb + 8 * (j >> 2) + hrow + (j & 3)];
   __syncthreads();  // histogram cleared; the loads above have completed
 
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
   float* srow = a.scores + (size_t)i * a.score_stride;
   const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  uint32_t lk[kScoreStages];
-#pragma unroll
-  for (int sidx = 0; sidx < kScoreStages; ++sidx)
-    lk[sidx] = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave][sidx]);
-  auto issue = [&](int it, uint32_t lds) {
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
+  auto issue = [&](int it, int sidx) {
     const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
     const int rel = p < k1 ? p : 0;
-    issue_rows<true>(kp, base, rel, lane, lds);
+    issue_tile<Kv, true>(a.k, base, rel, lane, wbase + sidx * Kv::kTileBytes);
   };
-  for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, lk[it]);
+  for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, it);
   for (int it = 0; it < ntw; ++it) {
     const int sidx = it % kScoreStages;
     // K(it) has landed once at most the groups issued after it are outstanding (score
     // stores issued meanwhile only make this wait longer, never shorter)
     const int later = min(ntw, it + kScoreStages) - (it + 1);
-    wait_vmcnt_dyn(later * kDmaPerHalf);
+    wait_vmcnt_n(later * Kv::kDma);
     bf16x8 kc[8];
-    read_k(sm.stage[wave][sidx], lane, kc);
-    if (it + kScoreStages < ntw) issue(it + kScoreStages, lk[sidx]);
+    read_k_of<Kv>(sm.stage[wave] + sidx * Kv::kTileBytes, lane, kc);
+    if (it + kScoreStages < ntw) issue(it + kScoreStages, sidx);
     f32x16 acc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -142,7 +145,13 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
 
 hipError_t launch_score_bf16(const ScoreArgs& a, const WorkList& wl, hipStream_t s) {
   const int grid = wl.n > 0 ? wl.n : a.b.total_q * a.n_split;
-  hipLaunchKernelGGL(score_bf16_kernel, dim3(grid), dim3(256), 0, s, a, wl);
+  hipLaunchKernelGGL(score_bf16_kernel<KvBf16>, dim3(grid), dim3(256), 0, s, a, wl);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_fp8kv(const ScoreArgs& a, const WorkList& wl, hipStream_t s) {
+  const int grid = wl.n > 0 ? wl.n : a.b.total_q * a.n_split;
+  hipLaunchKernelGGL(score_bf16_kernel<KvFp8>, dim3(grid), dim3(256), 0, s, a, wl);
   return hipGetLastError();
 }
 

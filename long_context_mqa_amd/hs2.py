@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhs2.so")
 
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
-HS2_BF16, HS2_F32 = 0, 1
+HS2_BF16, HS2_F32, HS2_FP8_E4M3 = 0, 1, 2
 MAX_TOP_K = 4096
 
 EXPORTED = [
@@ -31,6 +31,8 @@ EXPORTED = [
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
     "hs2_sparse_attn",
+    "hs2_full_attn_select_fp8kv",
+    "hs2_sparse_attn_fp8kv",
     "hs2_set_kernel_events",
 ]
 
@@ -85,6 +87,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_sparse_attn.restype = I32
     lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    lib.hs2_full_attn_select_fp8kv.restype = I32
+    lib.hs2_full_attn_select_fp8kv.argtypes = [SP, P, P, P, F, F, I32, I32, I32, I32, F, P, P, P, P, P, SZ, P]
+    lib.hs2_sparse_attn_fp8kv.restype = I32
+    lib.hs2_sparse_attn_fp8kv.argtypes = [SP, P, P, P, F, F, P, I32, I32, I32, I32, F, P, P, P, SZ, P]
     lib.hs2_set_kernel_events.restype = I32
     lib.hs2_set_kernel_events.argtypes = [P, I32]
     _lib = lib
@@ -152,16 +158,22 @@ class Batch:
                      np.ascontiguousarray(kl.numpy(), dtype=np.int32))
 
 
+def _size_code(dtype) -> int:
+    """dtype code of a workspace size query: torch.bfloat16, torch.float32 or "fp8" (FP8 K/V)."""
+    if isinstance(dtype, str) and dtype == "fp8":
+        return HS2_FP8_E4M3
+    return HS2_BF16 if dtype == torch.bfloat16 else HS2_F32
+
+
 def full_attn_select_workspace_size(batch: Batch, window: int, top_k: int, dtype=torch.bfloat16) -> int:
     b = batch.c()
     return int(load().hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, window, top_k,
-                                                          HS2_BF16 if dtype == torch.bfloat16 else HS2_F32))
+                                                          _size_code(dtype)))
 
 
 def sparse_attn_workspace_size(batch: Batch, window: int, top_k: int, dtype=torch.bfloat16) -> int:
     b = batch.c()
-    return int(load().hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k,
-                                                     HS2_BF16 if dtype == torch.bfloat16 else HS2_F32))
+    return int(load().hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k, _size_code(dtype)))
 
 
 def bridge_kv_workspace_size(d_model: int, n_layers: int, head_dim: int = 128) -> int:
@@ -257,3 +269,63 @@ def set_kernel_events(events: list | None) -> None:
     arr = (ctypes.c_void_p * len(events))(*events)
     set_kernel_events._keep = arr
     _check(lib.hs2_set_kernel_events(arr, len(events) // 2))
+
+
+def _fp8_codes(t: torch.Tensor) -> torch.Tensor:
+    if t.element_size() != 1 or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"FP8 K/V must be uint8 codes or torch.float8_e4m3fn (got {t.dtype})")
+    return t
+
+
+def full_attn_select_fp8kv(batch: Batch, q, k, v, k_scale: float, v_scale: float, window: int = 128,
+                           top_k: int = 1024, scale: float | None = None, out=None, lse=None, sel_idx=None,
+                           sel_count=None, workspace=None, stream=None, want_lse: bool = True):
+    """hs2_full_attn_select_fp8kv: the selector on an OCP FP8 E4M3 K/V cache with per-tensor
+    scales (q and out bf16). Returns (out, lse or None, sel_idx, sel_count)."""
+    lib = load()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    k, v = _fp8_codes(k), _fp8_codes(v)
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(batch.total_q, 64, dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty(batch.total_q, max(top_k, 0), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty(batch.total_q, dtype=torch.int32, device=dev)
+    b = batch.c()
+    need = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, window, top_k, HS2_FP8_E4M3)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check(lib.hs2_full_attn_select_fp8kv(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale),
+                                          q.shape[1], q.shape[2], window, top_k, scale, _ptr(out), _ptr(lse),
+                                          _ptr(sel_idx) if top_k > 0 else None, _ptr(sel_count), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
+    return out, lse, sel_idx, sel_count
+
+
+def sparse_attn_fp8kv(batch: Batch, q, k, v, k_scale: float, v_scale: float, sel_idx, window: int = 128,
+                      top_k: int | None = None, scale: float | None = None, out=None, lse=None, workspace=None,
+                      stream=None):
+    """hs2_sparse_attn_fp8kv: a sparse layer on the selector's FP8 E4M3 K/V cache. Returns (out, lse)."""
+    lib = load()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    k, v = _fp8_codes(k), _fp8_codes(v)
+    if top_k is None:
+        top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    b = batch.c()
+    need = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k, HS2_FP8_E4M3)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib.hs2_sparse_attn_fp8kv(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale),
+                                     _ptr(sel_idx) if top_k > 0 else None, q.shape[1], q.shape[2], window, top_k,
+                                     scale, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+    return out, lse

@@ -8,6 +8,8 @@ from .hs2_oracle import (  # noqa: F401
     block_query,
     bridge_kv,
     candidate_count,
+    dequantize_kv,
+    e4m3_decode,
     full_attention,
     logits,
     select_topk,

@@ -32,10 +32,35 @@ design notes of the repository):
   R6  sparse attention is a plain softmax over window U selected rows (no gate,
       no renormalisation against anything else).
   R7  KV Bridging is a plain linear map H @ W (no bias, norm or rotary embedding).
+  R8  an FP8 KV cache ([arex] "Numbers computed on three 80B-A3B models" accounts the
+      KV cache in FP8; the format is not named) holds OCP FP8 E4M3 codes with one
+      scale per tensor: row j stands for scale * decode(codes of row j).
 """
 from __future__ import annotations
 
 import numpy as np
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (R8), in float64.
+
+    The OCP 8-bit floating point specification, E4M3 encoding: bit 7 is the sign, bits
+    6..3 the exponent e (bias 7), bits 2..0 the mantissa m. e = 0 encodes the subnormals
+    (m/8) * 2^-6; otherwise the value is (1 + m/8) * 2^(e-7). The pattern e = 15, m = 7
+    (0x7F, 0xFF) is NaN; there are no infinities, so the largest finite value is
+    (1 + 6/8) * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def dequantize_kv(codes: np.ndarray, scale: float) -> np.ndarray:
+    """Rows of an FP8 KV cache as the values they stand for: scale * decode(codes) (R8)."""
+    return float(scale) * e4m3_decode(codes)
 
 
 def logits(q: np.ndarray, k_rows: np.ndarray, scale: float) -> np.ndarray:

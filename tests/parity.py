@@ -7,7 +7,11 @@ Comparison rules:
     ascending without duplicates. Without a tau (all candidates taken) the sets must
     be equal.
   * attention outputs (full and sparse): max |gpu - fp64| <= 1e-2 and mean <= 1e-3,
-    the GPU value taken in its output dtype.
+    the GPU value taken in its output dtype. With an FP8 K/V cache the mean is taken
+    over the error beyond each element's own output rounding, max(0, |gpu - fp64| -
+    ulp_bf16(fp64)/2): V's scale makes V's values non-representable in bf16, so even a
+    query with a single attended key (out = v_0) carries the bf16 rounding of |v| ~ 1
+    (mean ~1.1e-3), which a bf16 cache never has. The max rule is unchanged.
   * LSE: |gpu - fp64| <= 1e-3 (fp32 output of a value of magnitude ~10).
 """
 from __future__ import annotations
@@ -55,12 +59,19 @@ def check_selection(gpu_sel: np.ndarray, gpu_count: int, ref: dict, top_k: int, 
     return int(np.setdiff1d(sel, ref["sel"]).size)  # keys swapped inside the tolerance band
 
 
-def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half a bfloat16 unit in the last place at |x| (the bound of rounding x to bf16)."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 8.0)
+
+
+def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = "", beyond_rounding: bool = False):
     err = np.abs(gpu - ref)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     assert err.max() <= MAX_ABS, f"{what}: max abs err {err.max():.3e}"
-    assert err.mean() <= MEAN_ABS, f"{what}: mean abs err {err.mean():.3e}"
-    return float(err.max()), float(err.mean())
+    m = np.maximum(0.0, err - half_ulp_bf16(ref)) if beyond_rounding else err
+    assert m.mean() <= MEAN_ABS, f"{what}: mean abs err {m.mean():.3e}" + (" beyond rounding" if beyond_rounding else "")
+    return float(err.max()), float(m.mean())
 
 
 def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
@@ -68,13 +79,20 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
     assert err.max() <= LSE_ABS, f"{what}: lse max abs err {err.max():.3e}"
 
 
+def kv_to_f64(inp, rows: np.ndarray, scale: float) -> np.ndarray:
+    """Stored K or V rows as float64: FP8 codes through the oracle's own E4M3 decoding."""
+    if rows.dtype == np.uint8:
+        return oracle.dequantize_kv(rows, scale)
+    return stored_to_f64(rows)
+
+
 def oracle_query(inp, qi: int):
     """fp64 oracle of query qi's selector, from the stored inputs."""
     s = int(inp.q_seq[qi])
     a = int(inp.kv_start[s])
     t = int(inp.q_pos[qi])
-    K = stored_to_f64(inp.k[a:a + t + 1])
-    V = stored_to_f64(inp.v[a:a + t + 1])
+    K = kv_to_f64(inp, inp.k[a:a + t + 1], inp.spec.k_scale)
+    V = kv_to_f64(inp, inp.v[a:a + t + 1], inp.spec.v_scale)
     Q = stored_to_f64(inp.q_sel[qi])
     sp = inp.spec
     r = oracle.selector_query(Q, K, V, t, sp.window, sp.top_k, sp.scale)
@@ -87,8 +105,8 @@ def oracle_sparse(inp, qi: int, layer: int, sel: np.ndarray, K=None, V=None):
     a = int(inp.kv_start[s])
     t = int(inp.q_pos[qi])
     if K is None:
-        K = stored_to_f64(inp.k[a:a + t + 1])
-        V = stored_to_f64(inp.v[a:a + t + 1])
+        K = kv_to_f64(inp, inp.k[a:a + t + 1], inp.spec.k_scale)
+        V = kv_to_f64(inp, inp.v[a:a + t + 1], inp.spec.v_scale)
     Q = stored_to_f64(inp.q_sp[layer][qi])
     sp = inp.spec
     return oracle.sparse_attention(Q, K, V, t, sel, sp.window, sp.scale)

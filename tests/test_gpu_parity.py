@@ -15,7 +15,7 @@ from long_context_mqa_amd import hs2
 from tests.parity import (check_attn, check_lse, check_selection, from_dev, oracle_query, oracle_sparse,
                           to_dev)
 from workloads.configs import BlockSpec, block_config, make_block_inputs, make_bridge_inputs
-from workloads.gen import bf16_round, bf16_to_f32, stored_to_f64
+from workloads.gen import bf16_round, bf16_to_f32, e4m3_encode, stored_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -32,12 +32,21 @@ def run_block(inp, selector_only=False):
     k = to_dev(inp.k)
     v = to_dev(inp.v)
     q = to_dev(inp.q_sel)
-    out, lse, sel, cnt = hs2.full_attn_select(batch, q, k, v, sp.window, sp.top_k, sp.scale)
+    fp8 = sp.dtype == "fp8"
+    if fp8:
+        out, lse, sel, cnt = hs2.full_attn_select_fp8kv(batch, q, k, v, sp.k_scale, sp.v_scale, sp.window, sp.top_k,
+                                                        sp.scale)
+    else:
+        out, lse, sel, cnt = hs2.full_attn_select(batch, q, k, v, sp.window, sp.top_k, sp.scale)
     sparse = []
     if not selector_only:
         for l in range(sp.n_sparse):
             qs = to_dev(inp.q_sp[l])
-            o, _ = hs2.sparse_attn(batch, qs, k, v, sel, sp.window, sp.top_k, sp.scale)
+            if fp8:
+                o, _ = hs2.sparse_attn_fp8kv(batch, qs, k, v, sp.k_scale, sp.v_scale, sel, sp.window, sp.top_k,
+                                             sp.scale)
+            else:
+                o, _ = hs2.sparse_attn(batch, qs, k, v, sel, sp.window, sp.top_k, sp.scale)
             sparse.append(from_dev(o))
     torch.cuda.synchronize()
     return {"out": from_dev(out), "lse": from_dev(lse), "sel": sel.cpu().numpy(), "count": cnt.cpu().numpy(),
@@ -46,18 +55,19 @@ def run_block(inp, selector_only=False):
 
 def check_queries(inp, g, qis, what):
     sp = inp.spec
+    rr = sp.dtype == "fp8"  # FP8 K/V: the mean rule counts the error beyond the bf16 output rounding
     swapped = 0
     for qi in qis:
         r = oracle_query(inp, qi)
         t = r["t"]
         nc = oracle.candidate_count(t, sp.window)
         tag = f"{what} q{qi} t={t}"
-        check_attn(g["out"][qi], r["out"], tag + " selector out")
+        check_attn(g["out"][qi], r["out"], tag + " selector out", beyond_rounding=rr)
         check_lse(g["lse"][qi], r["lse"], tag)
         swapped += check_selection(g["sel"][qi], int(g["count"][qi]), r, sp.top_k, nc, tag)
         for l, o in enumerate(g["sparse"]):
             ref, _ = oracle_sparse(inp, qi, l, g["sel"][qi], r["K"], r["V"])
-            check_attn(o[qi], ref, tag + f" sparse layer {l}")
+            check_attn(o[qi], ref, tag + f" sparse layer {l}", beyond_rounding=rr)
     return swapped
 
 
@@ -99,13 +109,22 @@ def test_tiny_block_bf16():
     check_all_queries_properties(inp, g)
 
 
+def test_tiny_block_fp8():
+    """Workload 1's shape with an FP8 E4M3 K/V cache (per-tensor scales 0.05 and 0.03)."""
+    inp = make_block_inputs(block_config(1, dtype="fp8", seed=14))
+    _say("tiny fp8 block")
+    g = run_block(inp)
+    check_queries(inp, g, range(inp.spec.total_q), "tiny-fp8")
+    check_all_queries_properties(inp, g)
+
+
 RAGGED = BlockSpec(
     "ragged-small", [700, 1152, 1153, 3000, 9000, 40000],
     [[699, 100, 0], [1151], [1152], [2999, 2000], [8999, 5000, 127, 128, 1151, 1152], [39999]],
     dtype="bf16", n_sparse=2, needles_per_query=2, seed=12)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
 def test_ragged_small_contexts(dtype):
     """Several sequences and queries per sequence; t < window, candidates <= k and > k."""
     spec = BlockSpec(**{**RAGGED.__dict__, "dtype": dtype})
@@ -331,6 +350,10 @@ def test_workload3_decode_8x1m():
     _full(3, [0, 7])
 
 
+def test_workload6_decode_64x128k_fp8():
+    _full(6, [0, 41, 63])
+
+
 def test_workload4_chunk_4096_queries():
     _full(4, [0, 2048, 4095])
 
@@ -349,7 +372,7 @@ def test_workload5_bridge_and_ragged_decode():
     _full(5, [0, 13, 31])
 
 
-@pytest.mark.parametrize("shape", ["decode", "chunk"])
+@pytest.mark.parametrize("shape", ["decode", "chunk", "decode-fp8"])
 def test_logit_far_above_first_tile_is_recomputed(shape):
     """Keys whose logits for one head lie 150..402 (log2 units) above the other keys, at
     increasing positions over ~16 tiles: a wave whose first tile holds none of them (or
@@ -360,6 +383,10 @@ def test_logit_far_above_first_tile_is_recomputed(shape):
     if shape == "decode":
         spec = BlockSpec("spike-decode", [2000] * 40, [[1999]] * 40, dtype="bf16", n_sparse=1,
                          needles_per_query=0, seed=21)
+    elif shape == "decode-fp8":
+        # FP8 keys: a K scale large enough for the spike keys (components up to ~90)
+        spec = BlockSpec("spike-decode-fp8", [2000] * 40, [[1999]] * 40, dtype="fp8", n_sparse=1,
+                         needles_per_query=0, seed=23, k_scale=0.25)
     else:
         spec = BlockSpec("spike-chunk", [5000], [list(range(4990, 5000))], dtype="bf16", n_sparse=1,
                          needles_per_query=0, seed=22)
@@ -370,12 +397,17 @@ def test_logit_far_above_first_tile_is_recomputed(shape):
     unit = qh / np.linalg.norm(qh)
     c = spec.scale * math.log2(math.e) * np.linalg.norm(qh)  # x = c * alpha for k = alpha * unit
     pos = 1000 + 8 * np.arange(64)
+    fp8 = spec.dtype == "fp8"
     for j, pj in enumerate(pos):
-        inp.k[base + pj] = bf16_round(((150.0 + 4.0 * j) / c * unit).astype(np.float32))
+        key = ((150.0 + 4.0 * j) / c * unit).astype(np.float32)
+        inp.k[base + pj] = e4m3_encode(key, spec.k_scale) if fp8 else bf16_round(key)
     inp.q_sp[0][qi] = inp.q_sel[qi]
-    xs = spec.scale * math.log2(math.e) * (stored_to_f64(inp.k[base + pos]) @ qh)
-    assert xs.min() > 140.0 and np.all(np.diff(xs) > 0)
+    kk = oracle.dequantize_kv(inp.k[base + pos], spec.k_scale) if fp8 else stored_to_f64(inp.k[base + pos])
+    xs = spec.scale * math.log2(math.e) * (kk @ qh)
+    assert xs.min() > 140.0
+    if not fp8:  # FP8 rounding (2^-4 relative) may reorder neighbouring spikes
+        assert np.all(np.diff(xs) > 0)
     _say(f"spike {shape}: x in [{xs.min():.1f}, {xs.max():.1f}]")
     g = run_block(inp)
     check_queries(inp, g, range(spec.total_q), f"spike-{shape}")
-    assert int(pos[-1]) in set(g["sel"][qi].tolist())
+    assert int(pos[int(np.argmax(xs))]) in set(g["sel"][qi].tolist())

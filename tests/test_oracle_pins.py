@@ -315,3 +315,60 @@ def test_ties_prefer_smaller_position():
     assert s[3] > np.delete(s, [3, 7, 11, 15]).max()
     assert r["sel"].tolist() == [3, 7, 11]
     assert r["tau"] == s[3]
+
+
+# ----------------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache: the oracle's decoding of the codes
+# ----------------------------------------------------------------------------------
+
+def test_e4m3_decode_special_values():
+    """Values fixed by the OCP 8-bit floating point specification (E4M3: bias 7, 3
+    mantissa bits, subnormals, no infinities, S.1111.111 = NaN), written as closed forms."""
+    d = oracle.e4m3_decode
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+             0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+             0xB8: -1.0, 0xFE: -448.0}
+    got = d(np.array(list(cases), dtype=np.uint8))
+    assert got.tolist() == list(cases.values())
+    assert np.isnan(d(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+    z = d(np.array([0x80], dtype=np.uint8))[0]
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+
+
+def test_e4m3_decode_matches_torch_float8():
+    """All 256 codes against torch's float8_e4m3fn widening (a library routine)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_decode_order_and_symmetry():
+    """Codes 0x00..0x7E are the 127 non-negative finite values in increasing order, the
+    upper half their negatives, and the spacing doubles with each binade."""
+    d = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    pos = d[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(d[0x80:0xFF], -pos)
+    steps = np.diff(pos[8:])                    # normals: step 2^(e-10) inside binade e
+    for e in range(1, 15):
+        blk = steps[(e - 1) * 8:(e - 1) * 8 + 7]
+        assert np.all(blk == 2.0 ** (e - 10))
+
+
+def test_fp8_block_inputs_round_trip():
+    """The FP8 workload stores code(x / scale): decoding and rescaling returns x within
+    half a step of the format (relative 2^-4 for normals), and planted needle keys
+    survive as the largest logits of their head."""
+    spec = BlockSpec("fp8", [3000], [[2999]], dtype="fp8", n_sparse=0, needles_per_query=4, seed=31)
+    inp = make_block_inputs(spec)
+    assert inp.k.dtype == np.uint8 and inp.v.dtype == np.uint8 and inp.q_sel.dtype == np.uint16
+    K = oracle.dequantize_kv(inp.k, spec.k_scale)
+    assert np.isfinite(K).all() and np.abs(K).max() <= 448 * spec.k_scale
+    Q = stored_to_f64(inp.q_sel[0])
+    for (_, qi, h, p) in inp.needles:
+        s = Q[h] @ K.T * spec.scale
+        assert int(np.argmax(s)) == p

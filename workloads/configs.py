@@ -7,7 +7,8 @@ tokens, and 2,048-wide self-decoder hidden states for KV Bridging.
 Input recipe (identical for every workload; only sizes, dtype and seed change):
   * Q of the selector layer and of each sparse layer, K and V: N(0, std^2) drawn
     in float32 from chunk-seeded PCG64 streams, rounded to the stored dtype
-    (bfloat16 RNE, or kept float32).
+    (bfloat16 RNE, or kept float32). dtype "fp8": Q in bfloat16, K and V as OCP FP8
+    E4M3 codes of value / k_scale and value / v_scale (RNE, saturated at 448).
   * Needles: for needle n of global query i, head h = (needles_per_query*i + n)
     mod 64; the key row at position p is replaced by 12 * Q_sel[i, h] / |Q_sel[i, h]|
     (computed in float64 from the stored query, then rounded to the stored dtype),
@@ -23,7 +24,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .gen import bf16_round, bf16_to_f32, normal_f32, rng
+from .gen import bf16_round, bf16_to_f32, e4m3_encode, normal_f32, rng
 
 N_HEADS = 64
 HEAD_DIM = 128
@@ -45,7 +46,7 @@ class BlockSpec:
     name: str
     seq_lens: list[int]
     q_positions: list[list[int]]          # per sequence, the positions t of its queries
-    dtype: str = "bf16"                   # "bf16" or "f32"
+    dtype: str = "bf16"                   # "bf16", "f32" or "fp8" (FP8 E4M3 K/V, bf16 Q)
     n_sparse: int = 7
     needles_per_query: int = 8
     seed: int = 0
@@ -54,6 +55,8 @@ class BlockSpec:
     top_k: int = TOP_K
     n_heads: int = N_HEADS
     head_dim: int = HEAD_DIM
+    k_scale: float = 0.05                 # dtype "fp8": value = scale * E4M3 code value
+    v_scale: float = 0.03
 
     @property
     def total_q(self) -> int:
@@ -95,7 +98,11 @@ class BridgeInputs:
 
 
 def _stored(x: np.ndarray, dtype: str) -> np.ndarray:
-    return bf16_round(x) if dtype == "bf16" else x
+    return bf16_round(x) if dtype in ("bf16", "fp8") else x
+
+
+def _stored_kv(x: np.ndarray, spec: "BlockSpec", scale: float) -> np.ndarray:
+    return e4m3_encode(x, scale) if spec.dtype == "fp8" else _stored(x, spec.dtype)
 
 
 def _as_f32(x: np.ndarray) -> np.ndarray:
@@ -110,8 +117,8 @@ def make_block_inputs(spec: BlockSpec) -> BlockInputs:
     nq = spec.total_q
     s = spec.seed
 
-    k = _stored(normal_f32(s, _TAG_K, rows * d, spec.kv_std), spec.dtype).reshape(rows, d)
-    v = _stored(normal_f32(s, _TAG_V, rows * d, spec.kv_std), spec.dtype).reshape(rows, d)
+    k = _stored_kv(normal_f32(s, _TAG_K, rows * d, spec.kv_std), spec, spec.k_scale).reshape(rows, d)
+    v = _stored_kv(normal_f32(s, _TAG_V, rows * d, spec.kv_std), spec, spec.v_scale).reshape(rows, d)
     q_sel = _stored(normal_f32(s, _TAG_QSEL, nq * H * d), spec.dtype).reshape(nq, H, d)
     q_sp = [
         _stored(normal_f32(s, _TAG_QSP + l, nq * H * d), spec.dtype).reshape(nq, H, d)
@@ -149,7 +156,7 @@ def make_block_inputs(spec: BlockSpec) -> BlockInputs:
                 key = (NEEDLE_LOGIT * qv / np.linalg.norm(qv)).astype(np.float32)
                 p = int(pos[c])
                 c += 1
-                k[kv_start[si] + p] = _stored(key, spec.dtype)
+                k[kv_start[si] + p] = _stored_kv(key, spec, spec.k_scale)
                 needles.append((si, qi, h, p))
     return BlockInputs(spec, q_sel, q_sp, k, v, kv_start, kv_len, q_start, q_pos, q_seq, needles)
 
@@ -172,7 +179,10 @@ def ragged_lengths(seed: int, n_seqs: int, lo: int, hi: int) -> list[int]:
 
 
 def block_config(n: int, **over) -> BlockSpec:
-    """BlockSpec of workload n (1..5), with optional overrides (for scaled-down variants)."""
+    """BlockSpec of workload n (1..6), with optional overrides (for scaled-down variants).
+
+    Workload 6 is workload 2 on an FP8 E4M3 K/V cache (the first widening of the hot
+    path beyond the five workloads: the pages' KV accounting is FP8)."""
     if n == 1:
         spec = BlockSpec("tiny-4096-f32", [4096], [list(range(4080, 4096))], dtype="f32",
                          n_sparse=2, needles_per_query=8, seed=1)
@@ -192,6 +202,10 @@ def block_config(n: int, **over) -> BlockSpec:
         lens = ragged_lengths(5, 32, 4096, 524288)
         spec = BlockSpec("ragged-decode-32-4k-512k-bf16", lens, [[x - 1] for x in lens], n_sparse=7,
                          needles_per_query=8, seed=5, kv_std=math.sqrt(D_MODEL) * 0.02)
+    elif n == 6:
+        L = 131072
+        spec = BlockSpec("decode-64x128k-fp8kv", [L] * 64, [[L - 1]] * 64, dtype="fp8", n_sparse=7,
+                         needles_per_query=8, seed=6)
     else:
         raise ValueError(n)
     for key, val in over.items():

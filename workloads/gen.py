@@ -78,6 +78,17 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def e4m3_encode(x: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of x / scale in OCP FP8 E4M3 (round to nearest, ties to even), saturated at
+    +-448, the largest finite value; returned as uint8. Inputs must be finite. The
+    rounding is torch's float32 -> float8_e4m3fn conversion."""
+    import torch
+
+    y = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) / float(scale)
+    y.clamp_(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def stored_to_f64(a: np.ndarray) -> np.ndarray:
     """Widen stored values (bf16 bit patterns as uint16, or float32) to float64 exactly."""
     if a.dtype == np.uint16:
