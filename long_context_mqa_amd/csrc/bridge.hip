@@ -15,7 +15,9 @@
 // C^T = W^T H^T with eight waves, two per SIMD, of 64 rows x 192 (128) columns. The
 // wider tile re-reads each H row 2L/3 times instead of L times and moves 17% fewer
 // operand bytes per MFMA; the tile's 192 accumulator registers per lane still allow two
-// waves per SIMD. Operand tiles stream through three LDS stages by direct-to-LDS loads.
+// waves per SIMD. Operand tiles stream through two LDS stages 64 deep in the contraction
+// (80 KB each) by direct-to-LDS loads: one barrier per 64 of depth (half as many as with
+// 32-deep stages, which measured 15% slower on random data even with a third stage).
 // Tiles of the same rows run back to back on one XCD, so H is read from HBM once and
 // re-served from that XCD's L2 for the other column tiles.
 #include "hs2_internal.h"
@@ -51,14 +53,18 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(WPtrs wp, uint16_t* wt
   }
 }
 
-constexpr int kStagesG = 3;      // LDS stages of the contraction loop
-constexpr int kKStep = 32;       // contraction step (two MFMA k-steps of 16)
+constexpr int kStagesG = 2;      // LDS stages of the contraction loop
+constexpr int kKStep = 64;       // contraction depth per stage (four MFMA k-steps of 16)
+constexpr int kRowB = kKStep * 2;           // bytes of one operand row in a stage
+constexpr int kRowsPerCopy = 1024 / kRowB;  // rows filled by one wave-wide 16-byte copy
+constexpr int kLanesPerRow = 64 / kRowsPerCopy;
 
-// Operand tiles in LDS: rows of 64 bytes (32 bf16 of the contraction); the 16-byte chunk
-// c of row r sits at chunk position c ^ ((r >> 2) & 3), so that the eight lanes an LDS
-// read serves together (eight consecutive rows, same chunk) hit distinct banks.
+// Operand tiles in LDS: rows of 128 bytes (64 bf16 of the contraction); the 16-byte chunk
+// c of row r sits at chunk position c ^ ((r >> 1) & 7), so that the 16 lanes an LDS read
+// serves together (16 consecutive rows, same chunk) hit 16 distinct bank groups.
+__device__ inline int op_swz(int row) { return (row >> 1) & 7; }
 __device__ inline uint32_t op_off(int row, int chunk) {
-  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
+  return (uint32_t)(row * kRowB + ((chunk ^ op_swz(row)) << 4));
 }
 
 template <int N>
@@ -72,11 +78,11 @@ template <int kCols>
 __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a) {
   constexpr int kTA = kCols * kKStep * 2;        // W^T tile bytes per stage
   constexpr int kTB = kBM * kKStep * 2;          // H tile bytes per stage
-  constexpr int kCopA = kCols / 16 / kGWaves;    // 1 KB copies per wave per stage (16 rows each)
-  constexpr int kCopB = kBM / 16 / kGWaves;
-  constexpr int kGroup = kCopA + kCopB;          // copies issued per wave per stage
+  constexpr int kCopA = kCols / kRowsPerCopy / kGWaves;  // 1 KB copies per wave per stage
+  constexpr int kCopB = kBM / kRowsPerCopy / kGWaves;
   constexpr int kXB = kCols / 64;                // 32-column blocks per wave
-  static_assert(kCopA * 16 * kGWaves == kCols && kCopB * 16 * kGWaves == kBM, "copies must split evenly");
+  static_assert(kCopA * kRowsPerCopy * kGWaves == kCols && kCopB * kRowsPerCopy * kGWaves == kBM,
+                "copies must split evenly");
   __shared__ __align__(16) uint8_t lds_a[kStagesG][kTA];
   __shared__ __align__(16) uint8_t lds_b[kStagesG][kTB];
   const int lane = threadIdx.x & 63;
@@ -97,20 +103,21 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
 
   const uint32_t la0 = (uint32_t)(size_t)lds_a[0];
   const uint32_t lb0 = (uint32_t)(size_t)lds_b[0];
-  // this wave's copies: A copies kCopA*wave + q, B copies kCopB*wave + q, 16 rows each
+  // this wave's copies: A copies kCopA*wave + q, B copies kCopB*wave + q, kRowsPerCopy
+  // rows each; lane l fills chunk position l % kLanesPerRow of its row
   const uint16_t* ga[kCopA];
   const uint16_t* gb[kCopB];
 #pragma unroll
   for (int q = 0; q < kCopA; ++q) {
-    const int row = 16 * (kCopA * wave + q) + (lane >> 2);
-    ga[q] = wt + (size_t)row * a.d_model + ((lane & 3) ^ ((row >> 2) & 3)) * 8;
+    const int row = kRowsPerCopy * (kCopA * wave + q) + lane / kLanesPerRow;
+    ga[q] = wt + (size_t)row * a.d_model + ((lane % kLanesPerRow) ^ op_swz(row)) * 8;
   }
 #pragma unroll
   for (int q = 0; q < kCopB; ++q) {
-    const int row = 16 * (kCopB * wave + q) + (lane >> 2);
+    const int row = kRowsPerCopy * (kCopB * wave + q) + lane / kLanesPerRow;
     int64_t hr = r0 + row;
     if (hr >= a.n_rows) hr = a.n_rows - 1;
-    gb[q] = a.h + hr * a.d_model + ((lane & 3) ^ ((row >> 2) & 3)) * 8;
+    gb[q] = a.h + hr * a.d_model + ((lane % kLanesPerRow) ^ op_swz(row)) * 8;
   }
   auto issue = [&](int kt, int st) {
 #pragma unroll
@@ -127,18 +134,17 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
 
-  const int KT = a.d_model / kKStep;  // >= 2 (d_model is a multiple of 64)
+  const int KT = a.d_model / kKStep;  // >= 1 (d_model is a multiple of 64)
+  static_assert(kStagesG == 2, "the loop below keeps one stage in flight");
   issue(0, 0);
-  issue(1, 1);
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % kStagesG;
-    // this wave's copies of stage kt have landed once only those of stage kt+1 remain
-    if (kt + 1 < KT) wait_vm<kGroup>(); else wait_vm<0>();
+    wait_vm<0>();  // this wave's copies of stage kt have landed (the only ones in flight)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();  // the whole stage has landed; stage kt-1 is no longer read
-    if (kt + 2 < KT) issue(kt + 2, (kt + 2) % kStagesG);
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) % kStagesG);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kKStep / 16; ++ks) {
       const int c = 2 * ks + (lane >> 5);
       bf16x8 av[kXB], bv[2];
 #pragma unroll
