@@ -22,20 +22,36 @@ using namespace attn;
 // per-wave LDS stages (same swizzled layout and DMA as pass 1): 4 of bf16 tiles or 8 of
 // FP8 tiles, the same bytes in flight.
 // ------------------------------------------------------------------------------------
-constexpr int kScoreWaveBytes = 32768;  // LDS stage bytes per wave
+// LDS of a workgroup: 128 KB of K stages, the histogram and the staged scores (kSWaves x
+// 32 tiles x 32 keys of fp32, 16 KB).
+constexpr int kScoreStageBytes = 131072;
+constexpr int kSBufTiles = 128;  // tiles of scores staged per workgroup before they are written
 
-constexpr int kSFlush = 32;  // tiles of scores staged per wave before they are written
+// Waves per workgroup: 4 for bf16 tiles (one per SIMD; the pass is bound by HBM) and 8 for
+// FP8 tiles (two per SIMD), whose tiles arrive twice as fast per byte and would otherwise
+// leave one wave's MFMA, conversion and exp chain exposed; 186 registers per lane fit
+// two waves per SIMD.
+template <typename Kv>
+struct ScoreCfg {
+  static constexpr int kSWaves = Kv::kFp8 ? 8 : 4;
+  static constexpr int kWaveBytes = kScoreStageBytes / kSWaves;
+  static constexpr int kStages = kWaveBytes / Kv::kTileBytes;  // 4 bf16 or 4 FP8 tiles per wave
+  static constexpr int kSFlush = kSBufTiles / kSWaves;          // tiles staged per wave
+};
 
+template <int kSWaves, int kSFlush>
 struct ScoreSmem {
-  uint8_t stage[kWaves][kScoreWaveBytes];
+  uint8_t stage[kSWaves][kScoreStageBytes / kSWaves];
   uint32_t hist[kHistBins];
-  float sbuf[kWaves][kSFlush * kTile];
+  float sbuf[kSWaves][kSFlush * kTile];
 };
 
 template <typename Kv>
-__global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
-  constexpr int kScoreStages = kScoreWaveBytes / Kv::kTileBytes;
-  __shared__ __align__(16) ScoreSmem sm;
+__global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
+  constexpr int kSWaves = ScoreCfg<Kv>::kSWaves;
+  constexpr int kScoreStages = ScoreCfg<Kv>::kStages;
+  constexpr int kSFlush = ScoreCfg<Kv>::kSFlush;
+  __shared__ __align__(16) ScoreSmem<kSWaves, kSFlush> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int i, split;
@@ -76,10 +92,10 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
   __syncthreads();  // histogram cleared; the loads above have completed
 
   float* srow = a.scores + (size_t)i * a.score_stride;
-  const int ntw = wave < ntiles ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int ntw = wave < ntiles ? (ntiles - wave + kSWaves - 1) / kSWaves : 0;
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
   auto issue = [&](int it, int sidx) {
-    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
+    const int p = k0 + (wave + it * kSWaves) * kTile + (lane & 31);
     const int rel = p < k1 ? p : 0;
     issue_tile<Kv, true>(a.k, base, rel, lane, wbase + sidx * Kv::kTileBytes);
   };
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
     // lane l and l^32 hold complementary heads of the same key; add in a fixed order
     const float other = __shfl_xor(sum, 32);
     const float total = (lane < 32) ? sum + other : other + sum;
-    const int p = k0 + (wave + it * kWaves) * kTile + (lane & 31);
+    const int p = k0 + (wave + it * kSWaves) * kTile + (lane & 31);
     if (lane < 32 && p < k1) {
       sm.sbuf[wave][(it % kSFlush) * kTile + lane] = total;
       atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
@@ -121,7 +137,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
       const int nt = it + 1 - first;
       for (int e = lane; e < nt * 8; e += 64) {
         const int tt = first + e / 8;
-        const int q0 = k0 + (wave + tt * kWaves) * kTile + (e % 8) * 4;
+        const int q0 = k0 + (wave + tt * kSWaves) * kTile + (e % 8) * 4;
         const float4 v = *reinterpret_cast<const float4*>(&sm.sbuf[wave][(tt - first) * kTile + (e % 8) * 4]);
         if (q0 + 3 < k1) {
           *reinterpret_cast<float4*>(srow + q0) = v;
@@ -145,13 +161,13 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreArgs a, WorkList w
 
 hipError_t launch_score_bf16(const ScoreArgs& a, const WorkList& wl, hipStream_t s) {
   const int grid = wl.n > 0 ? wl.n : a.b.total_q * a.n_split;
-  hipLaunchKernelGGL(score_bf16_kernel<KvBf16>, dim3(grid), dim3(256), 0, s, a, wl);
+  hipLaunchKernelGGL(score_bf16_kernel<KvBf16>, dim3(grid), dim3(64 * ScoreCfg<KvBf16>::kSWaves), 0, s, a, wl);
   return hipGetLastError();
 }
 
 hipError_t launch_score_fp8kv(const ScoreArgs& a, const WorkList& wl, hipStream_t s) {
   const int grid = wl.n > 0 ? wl.n : a.b.total_q * a.n_split;
-  hipLaunchKernelGGL(score_bf16_kernel<KvFp8>, dim3(grid), dim3(256), 0, s, a, wl);
+  hipLaunchKernelGGL(score_bf16_kernel<KvFp8>, dim3(grid), dim3(64 * ScoreCfg<KvFp8>::kSWaves), 0, s, a, wl);
   return hipGetLastError();
 }
 
