@@ -7,7 +7,9 @@ selection) followed by every sparse layer of the hybrid block on the selector's 
 indices. The default workload is batched decode: 64 sequences x 131,072 cached tokens,
 one query each, 1 selector + 7 sparse layers (bf16). `--workload 3/4/5` measures the
 other workloads (5 also runs the KV Bridging projection of 1,048,576 hidden states);
-`--workload 6` is the default workload on an FP8 E4M3 K/V cache.
+`--workload 6` is the default workload on an FP8 E4M3 K/V cache; `--workload 7` is a
+prefill: KV Bridging of 262,144 hidden states, then exact causal attention of every one of
+the 262,144 positions (the self-decoder's full-attention layer, no selection).
 
 Prints ONE JSON line. Per-kernel durations come from HIP events recorded by the
 library around each kernel it launches, on the stream it launches on.
@@ -45,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -143,6 +145,8 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hs2.load()
+    if args.workload == 7:
+        return run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs)
     spec = block_config(args.workload)
     log(f"generating {spec.name}")
     inp = make_block_inputs(spec)
@@ -359,6 +363,93 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu baseline)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs) -> int:
+    """Workload 7: a step is the KV Bridging of N hidden states (3 layers) followed by the
+    exact causal attention of all N positions of one sequence (no selection)."""
+    import numpy as np
+    import torch
+
+    spec = block_config(7)
+    n = spec.total_rows
+    log(f"generating {spec.name}")
+    inp = make_block_inputs(spec)
+    dev = torch.device("cuda:0")
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, n, dev)
+    k, v, q = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel)
+    del inp
+    out = torch.empty_like(q)
+    lse = torch.empty(n, 64, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, hs2.causal_attn_workspace_size(batch)), dtype=torch.uint8, device=dev)
+    log(f"generating bridging inputs ({n} x 2048)")
+    bi = make_bridge_inputs(n, n_layers=3, seed=7)
+    h = to_dev(bi.h)
+    wk, wv = [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v]
+    ko = [torch.empty(n, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    vo = [torch.empty(n, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    bws = torch.empty(hs2.bridge_kv_workspace_size(2048, 3), dtype=torch.uint8, device=dev)
+    del bi
+    torch.cuda.synchronize()
+
+    def new_events(m):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(m)]
+        for e in evs:
+            e.record(torch.cuda.current_stream())
+        return evs
+
+    def step(ev_att=None, ev_br=None):
+        hs2.set_kernel_events([e.cuda_event for e in ev_br] if ev_br else None)   # slots: transpose, GEMM
+        hs2.bridge_kv(h, wk, wv, ko, vo, workspace=bws)
+        hs2.set_kernel_events([e.cuda_event for e in ev_att] if ev_att else None)  # slot 0: attention
+        hs2.causal_attn(batch, q, k, v, spec.scale, out=out, lse=lse, workspace=ws)
+        hs2.set_kernel_events(None)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(new_events(2), new_events(4)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(*evs[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    att_ms = float(np.mean([e[0][0].elapsed_time(e[0][1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1][2].elapsed_time(e[1][3]) for e in evs]))
+    pairs = n * (n + 1) // 2
+    f_att = pairs * QK_PV_FLOPS
+    f_br = 2 * n * 2048 * 256 * 3
+    ach = f_att / (att_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": n / (elapsed / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V and hidden states (bf16), weights N(0, 0.02^2)",
+        "config": {"workload": spec.name, "tokens": n, "queries": n, "q_heads": 64, "kv_heads": 1, "head_dim": 128,
+                   "bridging": {"rows": n, "d_model": 2048, "layers": 3}, "parallelism": "single GPU"},
+        "roofline": {"kernel": "attn_chunk (causal attention of every position, no selection)", "bound": "mfma",
+                     "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                     "traffic": None, "alg_flops_per_launch": f_att, "avg_launch_ms": att_ms},
+        "kernels_ms": {"causal_attn_pass1": att_ms, "bridge_gemm": gemm_ms},
+        "kernels_ms_source": "HIP events around the two kernels inside the timed steps",
+        "bridging": {"ms": gemm_ms, "tflops": f_br / (gemm_ms * 1e-3) / 1e12,
+                     "frac_mfma": f_br / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
     return 0
 

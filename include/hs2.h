@@ -183,6 +183,30 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
                            void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Exact causal attention of every query, without selection: the self-decoder's
+ * full-attention layer in prefill ([arex] "Outer KV Bridging, inner KV Reuse": prefill
+ * runs the self-decoder and the cross-decoder's KV projections; [toolnavs] "Prefill
+ * endet nach der Hälfte"), whose hidden states then feed hs2_bridge_kv:
+ *     out_h = sum_{j<=t} softmax_j(scale * <q_h, k_j>) v_j,   lse_h = log sum_{j<=t} exp(...)
+ * The batch is usually one sequence with every position as a query (q_pos = 0..n-1),
+ * but any descriptor accepted by hs2_full_attn_select is.
+ *
+ *   q        device [total_q][64][128], dtype dt (HS2_BF16 or HS2_F32)
+ *   k, v     device [total_kv_rows][128], dtype dt
+ *   scale    softmax scale, finite and > 0
+ *   out      device [total_q][64][128], dtype dt;  lse device [total_q][64] fp32 or NULL
+ *   workspace device scratch of hs2_causal_attn_workspace_size(...) bytes (0 when every
+ *            query's keys fit one workgroup), 256-byte aligned; contents on entry do
+ *            not matter
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_causal_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim,
+                                      hs2_dtype dt);
+
+hs2_status hs2_causal_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                           int32_t n_heads, int32_t head_dim, float scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * FP8 KV cache ([arex] "Numbers computed on three 80B-A3B models": the pages' KV-cache
  * accounting at 1M tokens stores K and V in FP8). The same two operations as
  * hs2_full_attn_select and hs2_sparse_attn, on a cache whose rows are OCP FP8 E4M3

@@ -164,8 +164,10 @@ __global__ __launch_bounds__(kCThreads) void attn_chunk_kernel(AttnArgs a, const
   __shared__ __align__(16) ChunkSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tix = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - tix * a.n_split;
+  // q-tiles in reverse list order: in a prefill the tiles of the last positions hold the
+  // most keys, and starting them first keeps the end of the launch from waiting on them
+  const int tix = (int)(gridDim.x / a.n_split) - 1 - (int)(blockIdx.x / a.n_split);
+  const int split = blockIdx.x % a.n_split;
   const int2 td = qtiles[tix];
   if (td.y <= 0) return;
   int i, t;
@@ -240,6 +242,32 @@ __global__ __launch_bounds__(kCThreads) void attn_chunk_kernel(AttnArgs a, const
     st.l[nb] += __shfl_xor(st.l[nb], 32);
     st.le[nb] += __shfl_xor(st.le[nb], 32);
   }
+  const int hrow = 4 * (lane >> 5);
+  if (a.direct) {
+    // one split per query: its output (normalised like the split combine with a single
+    // partial) and its LSE, straight from the wave's state; lane l holds head 32nb + l%32
+    __bf16* out = static_cast<__bf16*>(a.out) + (size_t)i * kHeads * kDim;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float inv = a.v_scale / st.l[nb];
+      __bf16* oh = out + (32 * nb + (lane & 31)) * kDim;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          __bf16 v4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v4[q] = (__bf16)(st.o[nb][mb][4 * jg + q] * inv);
+          *reinterpret_cast<uint2*>(oh + 32 * mb + 8 * jg + hrow) = __builtin_bit_cast(uint2, v4);
+        }
+      if (lane < 32) {
+        const float l2 = st.m[nb] + __log2f(st.le[nb]);
+        if (a.lse) a.lse[(size_t)i * kHeads + 32 * nb + lane] = l2 * kLn2;
+        if (a.lse2) a.lse2[(size_t)i * kHeads + 32 * nb + lane] = l2;
+      }
+    }
+    return;
+  }
   Partial* P = a.part + (size_t)i * a.n_split + split;
   if (lane < 32) {
 #pragma unroll
@@ -249,7 +277,6 @@ __global__ __launch_bounds__(kCThreads) void attn_chunk_kernel(AttnArgs a, const
       P->le[32 * nb + lane] = st.le[nb];
     }
   }
-  const int hrow = 4 * (lane >> 5);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll

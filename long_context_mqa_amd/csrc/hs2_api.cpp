@@ -129,7 +129,9 @@ struct SelectPlan {
          off_above = 0, off_cand = 0, total = 0;
 };
 
-SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
+// selection == false: exact causal attention only (hs2_causal_attn): no LSE copy, score
+// histograms or selection counters, and a query with one split gets its output directly.
+SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt, bool selection = true) {
   SelectPlan p;
   const int64_t tq = std::max(0, b->total_q);
   const int64_t max_cand = std::max<int64_t>(0, (int64_t)b->max_kv_len - window + 1);
@@ -160,13 +162,15 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
   p.score_stride = (max_cand + 63) / 64 * 64;
   size_t off = 0;
   p.off_part = off;
-  if (p.attn.n_split > 1 || p.chunk) off += align_up((size_t)tq * p.attn.n_split * sizeof(Partial));
-  p.off_lse2 = off;
-  off += align_up((size_t)tq * kHeads * sizeof(float));
-  p.off_hist = off;
-  off += align_up((size_t)tq * kHistBins * sizeof(uint32_t));
-  p.off_counters = off;
-  off += align_up((size_t)tq * 4 * sizeof(uint32_t));
+  if (p.attn.n_split > 1 || (p.chunk && selection)) off += align_up((size_t)tq * p.attn.n_split * sizeof(Partial));
+  if (selection) {
+    p.off_lse2 = off;
+    off += align_up((size_t)tq * kHeads * sizeof(float));
+    p.off_hist = off;
+    off += align_up((size_t)tq * kHistBins * sizeof(uint32_t));
+    p.off_counters = off;
+    off += align_up((size_t)tq * 4 * sizeof(uint32_t));
+  }
   if (p.chunk) {
     p.off_tiles = off;
     off += align_up((size_t)p.max_tiles * sizeof(int2));
@@ -528,9 +532,98 @@ hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   return ok();
 }
 
+// Exact causal attention of every query, no selection (the self-decoder's full-attention
+// layer in prefill): pass 1 alone, plus the split combine when a query's keys are split.
+hs2_status causal_impl(const hs2_seqs* batch, const void* q, const void* k, const void* v, int32_t n_heads,
+                       int32_t head_dim, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hs2_dtype dt, void* stream) {
+  if (dt == HS2_FP8_E4M3) return fail(HS2_ERR_UNSUPPORTED, "causal attention takes bf16 or fp32 K/V");
+  hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, 1, 0, scale, out, lse, dt);
+  if (st != HS2_OK) return st;
+  const SelectPlan p = plan_select(batch, 1, 0, dt, false);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
+                p.total);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (batch->total_q == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = dt == HS2_F32;
+  AttnArgs a{};
+  a.b = to_dev(batch);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sel = nullptr;
+  a.window = 1;
+  a.top_k = 0;
+  a.c2 = scale * kLog2e;
+  a.n_split = p.attn.n_split;
+  a.split_keys = p.attn.split_keys;
+  a.part = p.attn.n_split > 1 ? at<Partial>(workspace, p.off_part) : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.lse2 = nullptr;
+  a.v_scale = 1.0f;
+  a.direct = p.chunk && p.attn.n_split == 1;
+  const int grid = batch->total_q * p.attn.n_split;
+  LaunchMarks mk(s);
+  hipError_t e = hipSuccess;
+  int2* tiles = p.chunk ? at<int2>(workspace, p.off_tiles) : nullptr;
+  if (p.chunk) {
+    e = launch_qtile_prep(a.b, tiles, p.max_tiles, s);
+    if (e != hipSuccess) return hip_fail(e, "q-tile list launch");
+  }
+  e = mk.before(0);
+  if (e == hipSuccess) {
+    if (p.chunk)
+      e = launch_attn_chunk(a, tiles, p.max_tiles, s);
+    else if (f32)
+      e = launch_attn_f32(a, false, grid, nullptr, nullptr, s);
+    else
+      e = launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, nullptr, nullptr, s);
+  }
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "causal attention launch");
+  if (p.attn.n_split > 1) {
+    CombineArgs c{};
+    c.b = a.b;
+    c.part = a.part;
+    c.n_split = p.attn.n_split;
+    c.split_keys = p.attn.split_keys;
+    c.gather = 0;
+    c.window = 1;
+    c.top_k = 0;
+    c.out = out;
+    c.lse = lse;
+    c.lse2 = nullptr;
+    c.hist = nullptr;
+    c.counters = nullptr;
+    c.v_scale = 1.0f;
+    e = mk.before(1);
+    if (e == hipSuccess) e = launch_combine(c, f32, s);
+    if (e == hipSuccess) e = mk.after(1);
+    if (e != hipSuccess) return hip_fail(e, "split combine launch");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t hs2_causal_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t head_dim, hs2_dtype dt) {
+  (void)n_heads;
+  (void)head_dim;
+  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1) return 0;
+  return plan_select(batch, 1, 0, dt, false).total;
+}
+
+hs2_status hs2_causal_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v, int32_t n_heads,
+                           int32_t head_dim, float scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  return causal_impl(batch, q, k, v, n_heads, head_dim, scale, out, lse, workspace, workspace_bytes, dt, stream);
+}
 
 hs2_status hs2_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
                                 int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k,

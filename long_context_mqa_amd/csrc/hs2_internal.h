@@ -62,6 +62,7 @@ struct AttnArgs {
   float* lse;             // [total_q][64] natural log, nullable (n_split == 1)
   float* lse2;            // [total_q][64] log2 domain, nullable (n_split == 1)
   float v_scale;          // output factor (the V scale of FP8 storage; 1 otherwise)
+  int32_t direct;         // q-tile kernel with n_split == 1: write out/lse itself (no partials)
 };
 
 // (query, split) pairs of a launch in launch order: workgroup b takes item b, so that the

@@ -31,6 +31,8 @@ EXPORTED = [
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
     "hs2_sparse_attn",
+    "hs2_causal_attn_workspace_size",
+    "hs2_causal_attn",
     "hs2_full_attn_select_fp8kv",
     "hs2_sparse_attn_fp8kv",
     "hs2_set_kernel_events",
@@ -87,6 +89,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_sparse_attn.restype = I32
     lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    lib.hs2_causal_attn_workspace_size.restype = SZ
+    lib.hs2_causal_attn_workspace_size.argtypes = [SP, I32, I32, I32]
+    lib.hs2_causal_attn.restype = I32
+    lib.hs2_causal_attn.argtypes = [SP, P, P, P, I32, I32, F, P, P, P, SZ, I32, P]
     lib.hs2_full_attn_select_fp8kv.restype = I32
     lib.hs2_full_attn_select_fp8kv.argtypes = [SP, P, P, P, F, F, I32, I32, I32, I32, F, P, P, P, P, P, SZ, P]
     lib.hs2_sparse_attn_fp8kv.restype = I32
@@ -328,4 +334,29 @@ def sparse_attn_fp8kv(batch: Batch, q, k, v, k_scale: float, v_scale: float, sel
                                      _ptr(sel_idx) if top_k > 0 else None, q.shape[1], q.shape[2], window, top_k,
                                      scale, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                      _stream(stream)))
+    return out, lse
+
+
+def causal_attn_workspace_size(batch: Batch, dtype=torch.bfloat16) -> int:
+    b = batch.c()
+    return int(load().hs2_causal_attn_workspace_size(ctypes.byref(b), 64, 128, _size_code(dtype)))
+
+
+def causal_attn(batch: Batch, q, k, v, scale: float | None = None, out=None, lse=None, workspace=None, stream=None,
+                want_lse: bool = True):
+    """hs2_causal_attn: exact causal attention of every query (prefill, no selection).
+    Returns (out [total_q, 64, 128], lse [total_q, 64] or None)."""
+    lib = load()
+    dt = _dtype_code(q)
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(batch.total_q, 64, dtype=torch.float32, device=q.device)
+    b = batch.c()
+    need = lib.hs2_causal_attn_workspace_size(ctypes.byref(b), 64, 128, dt)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib.hs2_causal_attn(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), q.shape[1], q.shape[2], scale, _ptr(out),
+                               _ptr(lse), _ptr(workspace), workspace.numel(), dt, _stream(stream)))
     return out, lse

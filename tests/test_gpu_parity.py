@@ -275,6 +275,55 @@ def test_sparse_workspace_contents_do_not_matter():
         check_attn(outs[-1][qi], ref, f"ws q{qi}")
 
 
+# ----------------------------------------------------------------------------------
+# exact causal attention without selection (prefill of the self-decoder's full layer)
+# ----------------------------------------------------------------------------------
+
+def _causal_check(spec, qis, what):
+    inp = make_block_inputs(spec)
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, "cuda")
+    _say(f"causal {what}: {spec.total_q} queries")
+    o, lse = hs2.causal_attn(batch, to_dev(inp.q_sel), to_dev(inp.k), to_dev(inp.v), spec.scale)
+    torch.cuda.synchronize()
+    o, lse = from_dev(o), from_dev(lse)
+    for qi in qis:
+        s = int(inp.q_seq[qi])
+        a, t = int(inp.kv_start[s]), int(inp.q_pos[qi])
+        ref, ref_lse, _ = oracle.full_attention(stored_to_f64(inp.q_sel[qi]), stored_to_f64(inp.k[a:a + t + 1]),
+                                                stored_to_f64(inp.v[a:a + t + 1]), t, spec.scale)
+        check_attn(o[qi], ref, f"causal {what} q{qi} t={t}")
+        check_lse(lse[qi], ref_lse, f"causal {what} q{qi} t={t}")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_prefill_every_position(dtype):
+    """Two sequences with every position a query (q-tile kernel writing each query's
+    output itself for bf16; one query per workgroup for fp32)."""
+    spec = BlockSpec("prefill", [3000, 1500], [list(range(3000)), list(range(1500))], dtype=dtype, n_sparse=0,
+                     needles_per_query=0, seed=25)
+    _causal_check(spec, list(range(0, 4500, 37)) + [2999, 3000, 4499], f"prefill-{dtype}")
+
+
+def test_causal_split_keys():
+    """Few queries with long contexts: their keys are split over workgroups and merged by
+    the split combine, for the q-tile kernel (64 queries of one sequence) and for the
+    decode-shaped kernel (3 queries per sequence)."""
+    spec = BlockSpec("causal-qtile-split", [100000], [list(range(99936, 100000))], n_sparse=0, needles_per_query=0,
+                     seed=26)
+    _causal_check(spec, [0, 17, 63], "qtile-split")
+    spec = BlockSpec("causal-decode-split", [40000, 30000], [[39999, 20000, 5], [29999, 128, 0]], n_sparse=0,
+                     needles_per_query=0, seed=27)
+    _causal_check(spec, range(6), "decode-split")
+
+
+def test_workload7_prefill_262144():
+    """Workload 7's attention at full size: every position of a 262,144-token sequence."""
+    spec = block_config(7)
+    _causal_check(spec, [0, 1, 4095, 131071, 262142, 262143], spec.name)
+    torch.cuda.empty_cache()
+
+
 BRIDGE_ATOL = 2.0 ** -14
 
 

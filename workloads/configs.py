@@ -181,8 +181,10 @@ def ragged_lengths(seed: int, n_seqs: int, lo: int, hi: int) -> list[int]:
 def block_config(n: int, **over) -> BlockSpec:
     """BlockSpec of workload n (1..6), with optional overrides (for scaled-down variants).
 
-    Workload 6 is workload 2 on an FP8 E4M3 K/V cache (the first widening of the hot
-    path beyond the five workloads: the pages' KV accounting is FP8)."""
+    Workload 6 is workload 2 on an FP8 E4M3 K/V cache (the pages' KV accounting is FP8).
+    Workload 7 is a prefill: exact causal attention of every position of a 262,144-token
+    sequence (the self-decoder's full-attention layer), followed in the benchmark by the
+    KV Bridging of the same number of hidden states."""
     if n == 1:
         spec = BlockSpec("tiny-4096-f32", [4096], [list(range(4080, 4096))], dtype="f32",
                          n_sparse=2, needles_per_query=8, seed=1)
@@ -202,6 +204,9 @@ def block_config(n: int, **over) -> BlockSpec:
         lens = ragged_lengths(5, 32, 4096, 524288)
         spec = BlockSpec("ragged-decode-32-4k-512k-bf16", lens, [[x - 1] for x in lens], n_sparse=7,
                          needles_per_query=8, seed=5, kv_std=math.sqrt(D_MODEL) * 0.02)
+    elif n == 7:
+        L = 262144
+        spec = BlockSpec("prefill-262144-bf16", [L], [list(range(L))], n_sparse=0, needles_per_query=0, seed=7)
     elif n == 6:
         L = 131072
         spec = BlockSpec("decode-64x128k-fp8kv", [L] * 64, [[L - 1]] * 64, dtype="fp8", n_sparse=7,
