@@ -7,7 +7,9 @@ selection) followed by every sparse layer of the hybrid block on the selector's 
 indices. The default workload is batched decode: 64 sequences x 131,072 cached tokens,
 one query each, 1 selector + 7 sparse layers (bf16). `--workload 3/4/5` measures the
 other workloads (5 also runs the KV Bridging projection of 1,048,576 hidden states);
-`--workload 6` is the default workload on an FP8 E4M3 K/V cache; `--workload 7` is a
+`--workload 6` is the default workload on an FP8 E4M3 K/V cache; `--workload 8` is the
+default workload with the decode-time KV Bridging of the 64 new tokens into 3 layers'
+caches ahead of the selector; `--workload 7` is a
 prefill: KV Bridging of 262,144 hidden states, then exact causal attention of every one of
 the 262,144 positions (the self-decoder's full-attention layer, no selection).
 
@@ -47,7 +49,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -147,7 +149,8 @@ def main() -> int:
     hs2.load()
     if args.workload == 7:
         return run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs)
-    spec = block_config(args.workload)
+    append = args.workload == 8
+    spec = block_config(2 if append else args.workload)
     log(f"generating {spec.name}")
     inp = make_block_inputs(spec)
     dev = torch.device("cuda:0")
@@ -193,7 +196,22 @@ def main() -> int:
         bridge["vo"] = [torch.empty(1048576, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
         bridge["ws"] = torch.empty(hs2.bridge_kv_workspace_size(2048, 3), dtype=torch.uint8, device=dev)
         del bi
+    if append:
+        # decode-time bridging: the 64 new tokens' hidden states into the current-token
+        # rows of 3 layers' caches (layer 0's are the block's K and V)
+        log("generating the new tokens' hidden states and 3 layers' weights")
+        bi = make_bridge_inputs(nq, n_layers=3, seed=8)
+        app = {"h": to_dev(bi.h), "wk": [to_dev(w) for w in bi.w_k], "wv": [to_dev(w) for w in bi.w_v],
+               "rows": torch.from_numpy((inp.kv_start + inp.kv_len - 1).astype(np.int64)).to(dev)}
+        app["kc"] = [k] + [torch.empty_like(k) for _ in range(2)]
+        app["vc"] = [v] + [torch.empty_like(v) for _ in range(2)]
+        app["ws"] = torch.empty(max(1, hs2.bridge_kv_append_workspace_size(nq, 2048, 3)), dtype=torch.uint8,
+                                device=dev)
+        del bi
     torch.cuda.synchronize()
+
+    def append_call():
+        hs2.bridge_kv_append(app["h"], app["rows"], app["wk"], app["wv"], app["kc"], app["vc"], workspace=app["ws"])
 
     def new_events(n):
         """2n timing events plus a start marker; all recorded once so the HIP events exist."""
@@ -210,10 +228,13 @@ def main() -> int:
         evs[-1].record(torch.cuda.current_stream())   # start marker of this call
         hs2.set_kernel_events([e.cuda_event for e in evs[:-1]])
 
-    def step(ev_sel=None, ev_sp=None, ev_br=None):
+    def step(ev_sel=None, ev_sp=None, ev_br=None, ev_app=None):
         if bridge is not None:
             attach(ev_br)
             hs2.bridge_kv(bridge["h"], bridge["wk"], bridge["wv"], bridge["ko"], bridge["vo"], workspace=bridge["ws"])
+        if append:
+            attach(ev_app)
+            append_call()
         attach(ev_sel)
         select_call()
         for l in range(spec.n_sparse):
@@ -244,6 +265,8 @@ def main() -> int:
             hs2.bridge_kv(bridge["h"], bridge["wk"], bridge["wv"], bridge["ko"], bridge["vo"], workspace=bridge["ws"])
             hs2.set_kernel_events(None)
         else:
+            if append:
+                append_call()
             hs2.set_kernel_events([e.cuda_event for e in evs])      # slot 0: pass 1
         select_call()
         hs2.set_kernel_events(None)
@@ -265,7 +288,8 @@ def main() -> int:
     # Per-kernel breakdown: an instrumented pass after the timed steps (events around
     # every kernel), not part of the timed figure.
     n_prof = min(args.steps, 10)
-    ev = [(new_events(5), [new_events(2) for _ in range(spec.n_sparse)], new_events(2) if bridge else None)
+    ev = [(new_events(5), [new_events(2) for _ in range(spec.n_sparse)], new_events(2) if bridge else None,
+           new_events(1) if append else None)
           for _ in range(n_prof)]
     torch.cuda.synchronize()
     for s_ in range(n_prof):
@@ -287,6 +311,8 @@ def main() -> int:
         br = [e[2] for e in ev]
         kern["bridge_transpose"] = mean_ms(br, 0)
         kern["bridge_gemm"] = mean_ms(br, 1)
+    if append:
+        kern["bridge_append"] = mean_ms([e[3] for e in ev], 0)
     sparse_layer_ms = (kern.get("sparse_attn") or 0.0) + (kern.get("sparse_combine") or 0.0)
 
     # algorithmic work
@@ -321,6 +347,10 @@ def main() -> int:
     }
     if args.workload == 5:
         res["config"]["bridging"] = {"rows": 1048576, "d_model": 2048, "layers": 3}
+    if append:
+        res["config"]["workload"] = "decode-64x128k-bf16+bridging-append"
+        res["config"]["bridging_append"] = {"new_tokens": nq, "d_model": 2048, "layers": 3,
+                                            "weights_bytes": 3 * 2 * 2048 * 128 * 2}
     if fp8:
         res["config"]["kv_storage"] = {"format": "OCP FP8 E4M3", "k_scale": spec.k_scale, "v_scale": spec.v_scale,
                                        "compute": "codes converted exactly to bf16 for the MFMA"}

@@ -183,6 +183,35 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
                            void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Decode-time KV Bridging ([arex] "Outer KV Bridging, inner KV Reuse"): in decode each
+ * new token's hidden state h_i (the input of the matching self-decoder full-attention
+ * layer) goes through every bridged layer's own projections, and the results become
+ * that token's row of each layer's cache, before the selector of the step reads it:
+ *     K_l[rows[i]] = h_i W_K^l,   V_l[rows[i]] = h_i W_V^l,   i < n_new, l < n_layers
+ *
+ *   hidden     device [n_new][d_model] bf16
+ *   rows       device [n_new] int64: cache row of each new token; rows outside
+ *              [0, cache_rows) are not written; repeated rows are written in no set order
+ *   cache_rows host: rows of every cache (the bound of rows)
+ *   w_k, w_v   HOST arrays of n_layers DEVICE pointers, each [d_model][head_dim] bf16
+ *   k_cache,   HOST arrays of n_layers DEVICE pointers, each [cache_rows][head_dim] bf16;
+ *   v_cache    only the given rows are written (fp32 accumulation, round to nearest even)
+ *   workspace  device scratch of hs2_bridge_kv_append_workspace_size(...) bytes, 256-byte
+ *              aligned; contents on entry do not matter
+ *   Limits: dt == HS2_BF16; head_dim == 128; d_model a multiple of 128, <= 65536;
+ *           1 <= n_layers <= 8; 0 <= n_new <= 65536 (0 enqueues nothing).
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_bridge_kv_append_workspace_size(int32_t n_new, int32_t d_model, int32_t n_layers,
+                                           int32_t head_dim);
+
+hs2_status hs2_bridge_kv_append(const void* hidden, int32_t n_new, const int64_t* rows,
+                                int64_t cache_rows, int32_t d_model, int32_t n_layers,
+                                const void* const* w_k, const void* const* w_v,
+                                void* const* k_cache, void* const* v_cache, int32_t head_dim,
+                                void* workspace, size_t workspace_bytes, hs2_dtype dt,
+                                void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Exact causal attention of every query, without selection: the self-decoder's
  * full-attention layer in prefill ([arex] "Outer KV Bridging, inner KV Reuse": prefill
  * runs the self-decoder and the cross-decoder's KV projections; [toolnavs] "Prefill

@@ -676,6 +676,59 @@ size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, in
   return plan_sparse(batch, window, top_k).total;
 }
 
+size_t hs2_bridge_kv_append_workspace_size(int32_t n_new, int32_t d_model, int32_t n_layers, int32_t head_dim) {
+  if (n_new <= 0 || d_model <= 0 || n_layers <= 0 || head_dim <= 0) return 0;
+  return align_up((size_t)(d_model / kAppendSlice) * n_new * 2 * n_layers * head_dim * sizeof(float));
+}
+
+hs2_status hs2_bridge_kv_append(const void* hidden, int32_t n_new, const int64_t* rows, int64_t cache_rows,
+                                int32_t d_model, int32_t n_layers, const void* const* w_k, const void* const* w_v,
+                                void* const* k_cache, void* const* v_cache, int32_t head_dim, void* workspace,
+                                size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "bridging supports bf16 only");
+  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "bridging supports head_dim=128 only (got %d)", head_dim);
+  if (d_model < kAppendSlice || d_model > 65536 || d_model % kAppendSlice != 0)
+    return fail(HS2_ERR_UNSUPPORTED, "d_model must be a multiple of %d in [%d, 65536] (got %d)", kAppendSlice,
+                kAppendSlice, d_model);
+  if (n_layers < 1 || n_layers > 8) return fail(HS2_ERR_UNSUPPORTED, "n_layers must be in [1, 8] (got %d)", n_layers);
+  if (n_new < 0 || n_new > 65536) return fail(HS2_ERR_INVALID_ARG, "n_new must be in [0, 65536] (got %d)", n_new);
+  if (cache_rows < 0) return fail(HS2_ERR_INVALID_ARG, "cache_rows must be >= 0");
+  if (!w_k || !w_v || !k_cache || !v_cache) return fail(HS2_ERR_INVALID_ARG, "pointer arrays must not be NULL");
+  if (n_new > 0 && (!hidden || !rows)) return fail(HS2_ERR_INVALID_ARG, "hidden and rows must not be NULL");
+  if (!aligned(hidden, 16) || !aligned(rows, 8)) return fail(HS2_ERR_INVALID_ARG, "hidden must be 16-byte and rows 8-byte aligned");
+  AppendArgs a{};
+  for (int l = 0; l < n_layers; ++l) {
+    if (!w_k[l] || !w_v[l] || !k_cache[l] || !v_cache[l])
+      return fail(HS2_ERR_INVALID_ARG, "a weight or cache pointer of layer %d is NULL", l);
+    if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+      return fail(HS2_ERR_INVALID_ARG, "weights and caches must be 16-byte aligned (layer %d)", l);
+    a.w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    a.w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    a.outs[2 * l] = static_cast<uint16_t*>(k_cache[l]);
+    a.outs[2 * l + 1] = static_cast<uint16_t*>(v_cache[l]);
+  }
+  const size_t need = hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, head_dim);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes, need);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (n_new == 0) return ok();
+  a.h = static_cast<const uint16_t*>(hidden);
+  a.rows = rows;
+  a.part = static_cast<float*>(workspace);
+  a.cache_rows = cache_rows;
+  a.n_new = n_new;
+  a.d_model = d_model;
+  a.n_mats = 2 * n_layers;
+  a.n_slices = d_model / kAppendSlice;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess) e = launch_bridge_append(a, s);
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "bridging append launch");
+  return ok();
+}
+
 size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t head_dim) {
   if (d_model <= 0 || n_layers <= 0 || head_dim <= 0) return 0;
   return align_up((size_t)2 * n_layers * head_dim * d_model * sizeof(uint16_t));

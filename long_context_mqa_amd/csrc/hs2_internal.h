@@ -141,6 +141,22 @@ struct BridgeArgs {
   int32_t n_mats;
 };
 
+// Decode-time KV Bridging: the new tokens' hidden states through every bridged layer's
+// projections, written into the caches at the tokens' rows.
+constexpr int kAppendSlice = 128;  // contraction depth of one partial workgroup
+struct AppendArgs {
+  const uint16_t* h;       // [n_new][d_model] bf16
+  const int64_t* rows;     // device [n_new]: cache row of each new token
+  const uint16_t* w[16];   // n_mats weights [d_model][128] bf16 (K of layer l at 2l, V at 2l+1)
+  uint16_t* outs[16];      // n_mats caches [cache_rows][128] bf16
+  float* part;             // [n_slices][n_new][n_mats * 128] fp32 partial sums
+  int64_t cache_rows;
+  int32_t n_new;
+  int32_t d_model;
+  int32_t n_mats;
+  int32_t n_slices;        // d_model / kAppendSlice
+};
+
 // Resolves query i: sequence row base and position t. Returns false when the
 // descriptor is inconsistent (the query is then not computed). The sequence is first
 // guessed proportionally (exact for batches with equal query counts per sequence), and
@@ -211,5 +227,6 @@ hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s);
 hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats,
                                    uint16_t* wt, hipStream_t s);
 hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s);
+hipError_t launch_bridge_append(const AppendArgs& a, hipStream_t s);
 
 }  // namespace hs2

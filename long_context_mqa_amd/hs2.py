@@ -31,6 +31,8 @@ EXPORTED = [
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
     "hs2_sparse_attn",
+    "hs2_bridge_kv_append_workspace_size",
+    "hs2_bridge_kv_append",
     "hs2_causal_attn_workspace_size",
     "hs2_causal_attn",
     "hs2_full_attn_select_fp8kv",
@@ -89,6 +91,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_sparse_attn.restype = I32
     lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    lib.hs2_bridge_kv_append_workspace_size.restype = SZ
+    lib.hs2_bridge_kv_append_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.hs2_bridge_kv_append.restype = I32
+    lib.hs2_bridge_kv_append.argtypes = [P, I32, P, I64, I32, I32, P, P, P, P, I32, P, SZ, I32, P]
     lib.hs2_causal_attn_workspace_size.restype = SZ
     lib.hs2_causal_attn_workspace_size.argtypes = [SP, I32, I32, I32]
     lib.hs2_causal_attn.restype = I32
@@ -360,3 +366,26 @@ def causal_attn(batch: Batch, q, k, v, scale: float | None = None, out=None, lse
     _check(lib.hs2_causal_attn(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), q.shape[1], q.shape[2], scale, _ptr(out),
                                _ptr(lse), _ptr(workspace), workspace.numel(), dt, _stream(stream)))
     return out, lse
+
+
+def bridge_kv_append_workspace_size(n_new: int, d_model: int, n_layers: int, head_dim: int = 128) -> int:
+    return int(load().hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, head_dim))
+
+
+def bridge_kv_append(h, rows, w_k, w_v, k_cache, v_cache, workspace=None, stream=None):
+    """hs2_bridge_kv_append: K_l[rows[i]] = h_i W_K^l and V_l[rows[i]] = h_i W_V^l, written in
+    place into the caches (h [n_new, d_model] bf16, rows int64 [n_new] on the device)."""
+    lib = load()
+    n_layers = len(w_k)
+    n_new, d_model = int(h.shape[0]), int(h.shape[1])
+    assert rows.dtype == torch.int64 and rows.numel() == n_new
+    cache_rows = int(k_cache[0].shape[0])
+    assert all(int(c.shape[0]) == cache_rows for c in list(k_cache) + list(v_cache))
+    arr = ctypes.c_void_p * n_layers
+    need = lib.hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, 128)
+    if workspace is None:
+        workspace = _workspace(need, h.device)
+    _check(lib.hs2_bridge_kv_append(_ptr(h), n_new, _ptr(rows), cache_rows, d_model, n_layers,
+                                    arr(*[w.data_ptr() for w in w_k]), arr(*[w.data_ptr() for w in w_v]),
+                                    arr(*[c.data_ptr() for c in k_cache]), arr(*[c.data_ptr() for c in v_cache]),
+                                    128, _ptr(workspace), workspace.numel(), HS2_BF16, _stream(stream)))

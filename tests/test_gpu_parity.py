@@ -276,6 +276,65 @@ def test_sparse_workspace_contents_do_not_matter():
 
 
 # ----------------------------------------------------------------------------------
+# decode-time KV Bridging: new tokens' K/V rows written into the caches
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_new,d_model", [(37, 2048), (64, 256), (1, 128)])
+def test_bridge_append_rows(n_new, d_model):
+    """New tokens' projections into 3 layers' caches at scattered rows (two of them out of
+    range, which must be skipped); every other cache row keeps its bytes."""
+    bi = make_bridge_inputs(n_new, n_layers=3, seed=28 + n_new, d_model=d_model)
+    cache_rows = 3000
+    rows = np.random.default_rng(n_new).choice(cache_rows, n_new, replace=False).astype(np.int64)
+    if n_new > 8:
+        rows[5], rows[6] = cache_rows + 10, -1
+    g = torch.Generator().manual_seed(n_new)
+    init = [torch.randn(cache_rows, 128, generator=g).to(torch.bfloat16) for _ in range(6)]
+    caches = [c.cuda() for c in init]
+    hs2.bridge_kv_append(to_dev(bi.h), torch.from_numpy(rows).cuda(), [to_dev(w) for w in bi.w_k],
+                         [to_dev(w) for w in bi.w_v], caches[0::2], caches[1::2])
+    torch.cuda.synchronize()
+    valid = (rows >= 0) & (rows < cache_rows)
+    H = stored_to_f64(bi.h)
+    ks, vs = oracle.bridge_kv(H, [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v])
+    for l in range(3):
+        for c0, c, ref in ((init[2 * l], caches[2 * l], ks[l]), (init[2 * l + 1], caches[2 * l + 1], vs[l])):
+            got = from_dev(c)
+            keep = np.ones(cache_rows, bool)
+            keep[rows[valid]] = False
+            assert np.array_equal(got[keep], c0.float().numpy().astype(np.float64)[keep]), "a row not appended changed"
+            g_rows = got[rows[valid]]
+            r = ref[valid]
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+            assert np.all(np.abs(g_rows - r) <= ulp + BRIDGE_ATOL), f"layer {l}: appended rows beyond 1 bf16 ulp"
+
+
+def test_bridge_append_then_select():
+    """One decode step: the append writes each sequence's current-token K/V row of layer 0
+    (from that token's hidden state), then the selector and a sparse layer read the cache;
+    both match the oracle run on a cache holding the oracle's own projections there."""
+    spec = BlockSpec("append-step", [3000, 5000, 2200], [[2999], [4999], [2199]], n_sparse=1, needles_per_query=2,
+                     seed=29)
+    inp = make_block_inputs(spec)
+    bi = make_bridge_inputs(3, n_layers=1, seed=30)
+    rows = (inp.kv_start + inp.kv_len - 1).astype(np.int64)
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    hs2.bridge_kv_append(to_dev(bi.h), torch.from_numpy(rows).cuda(), [to_dev(bi.w_k[0])], [to_dev(bi.w_v[0])],
+                         [k], [v])
+    # the oracle's cache: the generator's rows, with the oracle's own projection at the new rows
+    ks, vs = oracle.bridge_kv(stored_to_f64(bi.h), [stored_to_f64(bi.w_k[0])], [stored_to_f64(bi.w_v[0])])
+    inp.k[rows] = bf16_round(ks[0].astype(np.float32))
+    inp.v[rows] = bf16_round(vs[0].astype(np.float32))
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, "cuda")
+    out, lse, sel, cnt = hs2.full_attn_select(batch, to_dev(inp.q_sel), k, v, spec.window, spec.top_k, spec.scale)
+    o1, _ = hs2.sparse_attn(batch, to_dev(inp.q_sp[0]), k, v, sel, spec.window, spec.top_k, spec.scale)
+    torch.cuda.synchronize()
+    g = {"out": from_dev(out), "lse": from_dev(lse), "sel": sel.cpu().numpy(), "count": cnt.cpu().numpy(),
+         "sparse": [from_dev(o1)]}
+    check_queries(inp, g, range(spec.total_q), "append-step")
+
+
+# ----------------------------------------------------------------------------------
 # exact causal attention without selection (prefill of the self-decoder's full layer)
 # ----------------------------------------------------------------------------------
 
