@@ -136,3 +136,67 @@ def test_workspace_sizes_follow_host_lengths(lib):
     s1 = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b1), 64, 128, 128, 1024, hs2.HS2_BF16)
     assert s0 > 0 and s1 > 0 and s0 % 256 == 0 and s1 % 256 == 0
     assert s0 != s1
+
+
+def test_fp8kv_rejects_bad_arguments(lib):
+    b = _batch()
+    ws = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, 128, 1024, hs2.HS2_FP8_E4M3)
+    assert ws > 0
+
+    def sel(ks=0.05, vs=0.03, hd=128, w=ws):
+        return lib.hs2_full_attn_select_fp8kv(ctypes.byref(b), FAKE, FAKE, FAKE, ks, vs, 64, hd, 128, 1024, 0.088,
+                                              FAKE * 2, None, FAKE * 3, None, FAKE, w, None)
+    assert sel(ks=0.0) == hs2.HS2_ERR_INVALID_ARG
+    assert sel(vs=float("inf")) == hs2.HS2_ERR_INVALID_ARG
+    assert b"k_scale" in lib.hs2_last_error()
+    assert sel(hd=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert sel(w=ws - 1) == hs2.HS2_ERR_WORKSPACE
+    # the bf16 entry points do not take FP8 K/V (they have no scales)
+    assert _select(lib, b, dt=hs2.HS2_FP8_E4M3, ws_bytes=ws) == hs2.HS2_ERR_UNSUPPORTED
+    assert b"fp8kv" in lib.hs2_last_error()
+    sws = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, 128, 1024, hs2.HS2_FP8_E4M3)
+    assert lib.hs2_sparse_attn_fp8kv(ctypes.byref(b), FAKE, FAKE, FAKE, -1.0, 0.03, FAKE * 3, 64, 128, 128, 1024,
+                                     0.088, FAKE * 2, None, FAKE, sws, None) == hs2.HS2_ERR_INVALID_ARG
+    assert lib.hs2_sparse_attn(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE * 3, 64, 128, 128, 1024, 0.088, FAKE * 2,
+                               None, FAKE, sws, hs2.HS2_FP8_E4M3, None) == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_causal_rejects_bad_arguments(lib):
+    b = _batch(total_q=4096, max_kv_len=4096, rows=4096)
+    b.max_q_per_seq = 4096
+    ws = lib.hs2_causal_attn_workspace_size(ctypes.byref(b), 64, 128, hs2.HS2_BF16)
+    call = lambda **kw: lib.hs2_causal_attn(ctypes.byref(b), FAKE, FAKE, FAKE, 64, kw.get("hd", 128),
+                                            kw.get("scale", 0.088), FAKE * 2, None, FAKE, kw.get("ws", ws),
+                                            kw.get("dt", hs2.HS2_BF16), None)
+    assert call(hd=256) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(scale=-1.0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(dt=hs2.HS2_FP8_E4M3) == hs2.HS2_ERR_UNSUPPORTED
+    if ws > 0:
+        assert call(ws=ws - 1) == hs2.HS2_ERR_WORKSPACE
+    # one sequence of 4,096 queries: q-tiles whose keys are not split need no partials,
+    # so the prefill workspace is only the q-tile list, far below the selector's
+    s_sel = lib.hs2_full_attn_select_workspace_size(ctypes.byref(b), 64, 128, 128, 1024, hs2.HS2_BF16)
+    assert ws < 64 * 1024 < s_sel
+
+
+def test_bridge_append_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p * 3
+    w = P(FAKE, FAKE, FAKE)
+    c = P(FAKE * 2, FAKE * 3, FAKE * 4)
+    ws = lib.hs2_bridge_kv_append_workspace_size(64, 2048, 3, 128)
+    assert ws == 2048 // 128 * 64 * 6 * 128 * 4
+    ok_args = dict(h=FAKE * 5, n=64, rows=FAKE * 6, cr=1 << 20, d=2048, L=3, hd=128, ws=ws, dt=0)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return lib.hs2_bridge_kv_append(a["h"], a["n"], a["rows"], a["cr"], a["d"], a["L"], w, w, c, c, a["hd"],
+                                        FAKE * 8, a["ws"], a["dt"], None)
+    assert call(dt=1) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(d=2000) == hs2.HS2_ERR_UNSUPPORTED       # not a multiple of 128
+    assert call(hd=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(n=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(n=70000) == hs2.HS2_ERR_INVALID_ARG
+    assert call(rows=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(rows=FAKE * 6 + 4) == hs2.HS2_ERR_INVALID_ARG  # misaligned
+    assert call(cr=-5) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws=ws - 4) == hs2.HS2_ERR_WORKSPACE
