@@ -267,6 +267,78 @@ hs2_status hs2_sparse_attn_fp8kv(const hs2_seqs* batch, const void* q, const voi
                                  void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * First-generation HySparse layout, the comparison variant ([arex] "Outer KV Bridging,
+ * inner KV Reuse": the predecessor selects its 1,024 global tokens as 64-token blocks and
+ * adds a separate 128-token sliding-window (SWA) branch fused through a gate; [arex]
+ * "Numbers computed on three 80B-A3B models": GQA, 64 query heads on 4 KV heads; [arex]
+ * "Lost points, the 290B check and open questions": the SWA branch has its own
+ * projections and local KV cache; [toolnavs] "Was HySparse2 tut": block-level selection).
+ *
+ * Layout: K and V rows hold the 4 KV heads, [total_kv_rows][4][128] bf16; query head h
+ * reads KV head h / 16. A block is the 64 positions 64b .. 64b+63 of a sequence.
+ *
+ * Selector (exact causal attention plus block selection), query i at position t:
+ *     out_h = sum_{j<=t} softmax_j(scale * <q_h, k_{j,h/16}>) v_{j,h/16},  lse_h as above
+ *     score_{g,b} = sum over the 16 heads h of KV head g of the softmax probabilities of
+ *                   the positions j <= t of block b,   b = 0 .. t/64
+ *     blk_idx[i][g] = the top_blocks best blocks of KV head g (all of them if t/64 + 1 <=
+ *                   top_blocks), ties to the smaller index, ascending, padded with -1;
+ *     blk_count[i][g] = min(top_blocks, t/64 + 1)
+ *
+ *   q        device [total_q][64][128] bf16;  k, v device [total_kv_rows][4][128] bf16
+ *   out      device [total_q][64][128] bf16;  lse device [total_q][64] fp32 or NULL
+ *   blk_idx  device [total_q][4][top_blocks] int32; blk_count device [total_q][4] or NULL
+ *   workspace device scratch of hs2_v1_full_attn_select_workspace_size(...) bytes, 256-byte
+ *            aligned, contents on entry irrelevant
+ *   Limits: dt == HS2_BF16, n_heads == 64, n_kv_heads == 4, head_dim == 128,
+ *           1 <= top_blocks <= 64, max_kv_len <= 2^21. A query whose position lies beyond
+ *           max_kv_len is treated as an inconsistent descriptor (NaN outputs, counts -1).
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_v1_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_heads,
+                                              int32_t n_kv_heads, int32_t head_dim,
+                                              int32_t top_blocks, hs2_dtype dt);
+
+hs2_status hs2_v1_full_attn_select(const hs2_seqs* batch, const void* q, const void* k,
+                                   const void* v, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t top_blocks, float scale, void* out,
+                                   float* lse, int32_t* blk_idx, int32_t* blk_count,
+                                   void* workspace, size_t workspace_bytes, hs2_dtype dt,
+                                   void* stream);
+
+/* Sparse layer of the v1 layout, query i at position t, head h of KV head g = h / 16:
+ *     o_sparse_h = softmax attention over the positions j <= t of the blocks
+ *                  blk_idx[i][g][*] (entries < 0 or > t/64 are ignored; entries must be
+ *                  distinct) on the shared cache k, v
+ *     o_swa_h    = softmax attention over positions max(0, t-window+1) .. t of this
+ *                  layer's own cache k_swa, v_swa
+ *     out_h      = gate_sparse[i][h] * o_sparse_h + gate_swa[i][h] * o_swa_h
+ * A branch without attended positions contributes zero.
+ *
+ *   k, v          the selector's cache, device [total_kv_rows][4][128] bf16
+ *   blk_idx       device [total_q][4][top_blocks] int32 (the selector's output)
+ *   k_swa, v_swa  device [num_seqs][swa_slots][4][128] bf16: a ring per sequence, position p
+ *                 of sequence s in row s * swa_slots + p % swa_slots. Every position a query
+ *                 reads must be present: swa_slots >= window plus the spread of the
+ *                 positions of one sequence's queries.
+ *   gate_sparse,  device [total_q][64] fp32: the gate values of the two branches (how they
+ *   gate_swa      are computed is the caller's)
+ *   out           device [total_q][64][128] bf16
+ *   workspace     device scratch of hs2_v1_sparse_attn_workspace_size(...) bytes
+ *   Limits: as for the selector; 1 <= window <= swa_slots <= 2^20.
+ * ------------------------------------------------------------------------------------ */
+size_t hs2_v1_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads,
+                                         int32_t n_kv_heads, int32_t head_dim,
+                                         int32_t top_blocks, hs2_dtype dt);
+
+hs2_status hs2_v1_sparse_attn(const hs2_seqs* batch, const void* q, const void* k,
+                              const void* v, const int32_t* blk_idx, int32_t top_blocks,
+                              const void* k_swa, const void* v_swa, int32_t swa_slots,
+                              int32_t window, const float* gate_sparse, const float* gate_swa,
+                              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                              void* out, void* workspace, size_t workspace_bytes, hs2_dtype dt,
+                              void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Kernel timing hook, for benchmarks and profilers that need per-kernel durations on the
  * library's own stream (not an operation of the method). While attached, every hs2_*
  * compute call records events[2*j] right before and events[2*j+1] right after its
@@ -275,6 +347,8 @@ hs2_status hs2_sparse_attn_fp8kv(const hs2_seqs* batch, const void* q, const voi
  *                         4 top-k finish
  *   hs2_sparse_attn:      0 attention, 1 split combine
  *   hs2_bridge_kv:        0 weight transpose, 1 fan-out GEMM
+ *   hs2_v1_full_attn_select: 0 attention, 1 combine and block selection
+ *   hs2_v1_sparse_attn:      0 attention (both branches), 1 gated combine
  * A slot whose kernel a call does not need (e.g. no split combine when one workgroup
  * covers a query) is not recorded. The events are hipEvent_t handles created and owned
  * by the caller and must stay valid while attached. events == NULL or n_pairs == 0

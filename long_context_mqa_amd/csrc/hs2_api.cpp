@@ -9,6 +9,7 @@
 
 #include "hs2.h"
 #include "hs2_internal.h"
+#include "v1_internal.h"
 
 
 namespace {
@@ -780,6 +781,208 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
   if (e == hipSuccess) e = launch_bridge_gemm(a, s);
   if (e == hipSuccess) e = mk.after(1);
   if (e != hipSuccess) return hip_fail(e, "bridging launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------
+// First-generation HySparse layout (GQA 64:4, 64-token block selection, gated window
+// branch): the comparison variant.
+// ------------------------------------------------------------------------------------
+namespace {
+
+struct V1SelPlan {
+  int n_split = 1, units = 1, stride = 1;
+  size_t off_blse = 0, total = 0;
+};
+
+// Parts of 'units' blocks per query so that the launch holds about four workgroups per
+// CU (one resident at a time: 128 KB of LDS each), at most kMaxSplit parts per query.
+V1SelPlan plan_v1_select(const hs2_seqs* b) {
+  V1SelPlan p;
+  const int64_t tq = std::max(0, b->total_q);
+  const int64_t nblk = ceil_div(std::max(1, b->max_kv_len), kV1Block);
+  int64_t u = std::max<int64_t>(2, ceil_div(std::max<int64_t>(1, tq * nblk), 4 * kTargetGroups));
+  u = std::max<int64_t>(u, ceil_div(nblk, kMaxSplit));
+  p.n_split = (int)ceil_div(nblk, u);
+  p.units = (int)ceil_div(nblk, p.n_split);  // rebalanced: n_split * units < nblk + n_split
+  p.stride = p.n_split * p.units;  // blocks the parts cover (>= the blocks of max_kv_len)
+  p.off_blse = align_up((size_t)tq * kV1Groups * p.n_split * sizeof(V1Partial));
+  p.total = p.off_blse + align_up((size_t)tq * kV1Groups * p.stride * kV1GroupHeads * sizeof(float));
+  return p;
+}
+
+constexpr int kV1SparseUnits = 2;  // block slots per sparse part (4 tiles, as the window part)
+
+struct V1SpPlan {
+  int n_split = 2;
+  size_t total = 0;
+};
+
+V1SpPlan plan_v1_sparse(const hs2_seqs* b, int top_blocks) {
+  V1SpPlan p;
+  const int64_t tq = std::max(0, b->total_q);
+  p.n_split = (int)ceil_div(std::max(1, top_blocks), kV1SparseUnits) + 1;
+  p.total = align_up((size_t)tq * kV1Groups * p.n_split * sizeof(V1Partial));
+  return p;
+}
+
+hs2_status check_v1_common(const hs2_seqs* b, const void* q, const void* k, const void* v, int32_t n_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t top_blocks, float scale, const void* out,
+                           hs2_dtype dt) {
+  hs2_status st = check_batch(b);
+  if (st != HS2_OK) return st;
+  if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "the v1 layout supports bf16 only (dtype %d)", (int)dt);
+  if (n_heads != kHeads || n_kv_heads != kV1Groups || head_dim != kDim)
+    return fail(HS2_ERR_UNSUPPORTED, "only n_heads=64, n_kv_heads=4, head_dim=128 are supported (got %d, %d, %d)",
+                n_heads, n_kv_heads, head_dim);
+  if (b->max_kv_len > kV1MaxBlocks * kV1Block)
+    return fail(HS2_ERR_UNSUPPORTED, "max_kv_len must be <= %d for the v1 layout (got %d)", kV1MaxBlocks * kV1Block,
+                b->max_kv_len);
+  if (top_blocks < 1 || top_blocks > kV1MaxTopBlocks)
+    return fail(HS2_ERR_INVALID_ARG, "top_blocks must be in [1, %d] (got %d)", kV1MaxTopBlocks, top_blocks);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(HS2_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (b->total_q > 0 && (!q || !out)) return fail(HS2_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (b->total_kv_rows > 0 && (!k || !v)) return fail(HS2_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(HS2_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (out && (out == q || out == k || out == v)) return fail(HS2_ERR_INVALID_ARG, "out aliases an input");
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hs2_v1_full_attn_select_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t n_kv_heads,
+                                              int32_t head_dim, int32_t top_blocks, hs2_dtype dt) {
+  (void)n_heads;
+  (void)n_kv_heads;
+  (void)head_dim;
+  (void)top_blocks;
+  (void)dt;
+  if (!batch || batch->total_q < 0 || batch->max_kv_len < 1) return 0;
+  return plan_v1_select(batch).total;
+}
+
+hs2_status hs2_v1_full_attn_select(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                   int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t top_blocks,
+                                   float scale, void* out, float* lse, int32_t* blk_idx, int32_t* blk_count,
+                                   void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  hs2_status st = check_v1_common(batch, q, k, v, n_heads, n_kv_heads, head_dim, top_blocks, scale, out, dt);
+  if (st != HS2_OK) return st;
+  if (batch->total_q > 0 && !blk_idx) return fail(HS2_ERR_INVALID_ARG, "blk_idx must not be NULL");
+  if ((blk_idx && !aligned(blk_idx, 4)) || (blk_count && !aligned(blk_count, 4)) || (lse && !aligned(lse, 4)))
+    return fail(HS2_ERR_INVALID_ARG, "blk_idx, blk_count and lse must be 4-byte aligned");
+  const V1SelPlan p = plan_v1_select(batch);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
+                p.total);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (batch->total_q == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  V1AttnArgs a{};
+  a.b = to_dev(batch);
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.c2 = scale * kLog2e;
+  a.n_split = p.n_split;
+  a.split_units = p.units;
+  a.part = static_cast<V1Partial*>(workspace);
+  a.blse = at<float>(workspace, p.off_blse);
+  a.blse_stride = p.stride;
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess) e = launch_v1_attn(a, false, batch->total_q * p.n_split, s);
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "v1 attention launch");
+  V1SelectArgs c{};
+  c.b = a.b;
+  c.part = a.part;
+  c.n_split = p.n_split;
+  c.split_units = p.units;
+  c.blse = a.blse;
+  c.blse_stride = p.stride;
+  c.out = static_cast<__bf16*>(out);
+  c.lse = lse;
+  c.blk_idx = blk_idx;
+  c.blk_count = blk_count;
+  c.top_blocks = top_blocks;
+  e = mk.before(1);
+  if (e == hipSuccess) e = launch_v1_select(c, s);
+  if (e == hipSuccess) e = mk.after(1);
+  if (e != hipSuccess) return hip_fail(e, "v1 combine and block selection launch");
+  return ok();
+}
+
+size_t hs2_v1_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, int32_t n_kv_heads,
+                                         int32_t head_dim, int32_t top_blocks, hs2_dtype dt) {
+  (void)n_heads;
+  (void)n_kv_heads;
+  (void)head_dim;
+  (void)dt;
+  if (!batch || batch->total_q < 0 || top_blocks < 1) return 0;
+  return plan_v1_sparse(batch, top_blocks).total;
+}
+
+hs2_status hs2_v1_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                              const int32_t* blk_idx, int32_t top_blocks, const void* k_swa, const void* v_swa,
+                              int32_t swa_slots, int32_t window, const float* gate_sparse, const float* gate_swa,
+                              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale, void* out,
+                              void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream) {
+  hs2_status st = check_v1_common(batch, q, k, v, n_heads, n_kv_heads, head_dim, top_blocks, scale, out, dt);
+  if (st != HS2_OK) return st;
+  if (window < 1 || swa_slots < window || swa_slots > (1 << 20))
+    return fail(HS2_ERR_INVALID_ARG, "need 1 <= window <= swa_slots <= 2^20 (got window %d, swa_slots %d)", window,
+                swa_slots);
+  if (batch->total_q > 0 && (!blk_idx || !k_swa || !v_swa || !gate_sparse || !gate_swa))
+    return fail(HS2_ERR_INVALID_ARG, "blk_idx, k_swa, v_swa, gate_sparse and gate_swa must not be NULL");
+  if (!aligned(k_swa, 16) || !aligned(v_swa, 16) || !aligned(blk_idx, 4) || !aligned(gate_sparse, 4) ||
+      !aligned(gate_swa, 4))
+    return fail(HS2_ERR_INVALID_ARG, "k_swa and v_swa must be 16-byte aligned, blk_idx and the gates 4-byte");
+  if (out && (out == k_swa || out == v_swa)) return fail(HS2_ERR_INVALID_ARG, "out aliases an input");
+  const V1SpPlan p = plan_v1_sparse(batch, top_blocks);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
+                p.total);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (batch->total_q == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  V1AttnArgs a{};
+  a.b = to_dev(batch);
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.k_swa = static_cast<const __bf16*>(k_swa);
+  a.v_swa = static_cast<const __bf16*>(v_swa);
+  a.swa_slots = swa_slots;
+  a.window = window;
+  a.blk = blk_idx;
+  a.top_blocks = top_blocks;
+  a.c2 = scale * kLog2e;
+  a.n_split = p.n_split;
+  a.split_units = kV1SparseUnits;
+  a.part = static_cast<V1Partial*>(workspace);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess) e = launch_v1_attn(a, true, batch->total_q * p.n_split, s);
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "v1 sparse attention launch");
+  V1GateArgs c{};
+  c.b = a.b;
+  c.part = a.part;
+  c.n_split = p.n_split;
+  c.gate_sparse = gate_sparse;
+  c.gate_swa = gate_swa;
+  c.out = static_cast<__bf16*>(out);
+  e = mk.before(1);
+  if (e == hipSuccess) e = launch_v1_gate(c, s);
+  if (e == hipSuccess) e = mk.after(1);
+  if (e != hipSuccess) return hip_fail(e, "v1 gated combine launch");
   return ok();
 }
 

@@ -38,6 +38,10 @@ EXPORTED = [
     "hs2_full_attn_select_fp8kv",
     "hs2_sparse_attn_fp8kv",
     "hs2_set_kernel_events",
+    "hs2_v1_full_attn_select_workspace_size",
+    "hs2_v1_full_attn_select",
+    "hs2_v1_sparse_attn_workspace_size",
+    "hs2_v1_sparse_attn",
 ]
 
 
@@ -105,6 +109,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_fp8kv.argtypes = [SP, P, P, P, F, F, P, I32, I32, I32, I32, F, P, P, P, SZ, P]
     lib.hs2_set_kernel_events.restype = I32
     lib.hs2_set_kernel_events.argtypes = [P, I32]
+    lib.hs2_v1_full_attn_select_workspace_size.restype = SZ
+    lib.hs2_v1_full_attn_select_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
+    lib.hs2_v1_full_attn_select.restype = I32
+    lib.hs2_v1_full_attn_select.argtypes = [SP, P, P, P, I32, I32, I32, I32, F, P, P, P, P, P, SZ, I32, P]
+    lib.hs2_v1_sparse_attn_workspace_size.restype = SZ
+    lib.hs2_v1_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
+    lib.hs2_v1_sparse_attn.restype = I32
+    lib.hs2_v1_sparse_attn.argtypes = [SP, P, P, P, P, I32, P, P, I32, I32, P, P, I32, I32, I32, F, P, P, SZ, I32, P]
     _lib = lib
     return lib
 
@@ -389,3 +401,74 @@ def bridge_kv_append(h, rows, w_k, w_v, k_cache, v_cache, workspace=None, stream
                                     arr(*[w.data_ptr() for w in w_k]), arr(*[w.data_ptr() for w in w_v]),
                                     arr(*[c.data_ptr() for c in k_cache]), arr(*[c.data_ptr() for c in v_cache]),
                                     128, _ptr(workspace), workspace.numel(), HS2_BF16, _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------
+# First-generation HySparse layout (the comparison variant): GQA 64:4, 64-token block
+# selection per KV head, gated sliding-window branch.
+# ------------------------------------------------------------------------------------
+V1_KV_HEADS = 4
+
+
+def v1_full_attn_select_workspace_size(batch: Batch, top_blocks: int = 16) -> int:
+    b = batch.c()
+    return int(load().hs2_v1_full_attn_select_workspace_size(ctypes.byref(b), 64, V1_KV_HEADS, 128, top_blocks,
+                                                             HS2_BF16))
+
+
+def v1_full_attn_select(batch: Batch, q, k, v, top_blocks: int = 16, scale: float | None = None, out=None,
+                        lse=None, blk_idx=None, blk_count=None, workspace=None, stream=None, want_lse: bool = True):
+    """hs2_v1_full_attn_select: exact causal GQA attention (k, v [rows, 4, 128]) plus the
+    top_blocks 64-token blocks of each KV head.
+
+    Returns (out [total_q, 64, 128], lse [total_q, 64] or None, blk_idx [total_q, 4, top_blocks],
+    blk_count [total_q, 4]).
+    """
+    lib = load()
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(batch.total_q, 64, dtype=torch.float32, device=dev)
+    if blk_idx is None:
+        blk_idx = torch.empty(batch.total_q, V1_KV_HEADS, top_blocks, dtype=torch.int32, device=dev)
+    if blk_count is None:
+        blk_count = torch.empty(batch.total_q, V1_KV_HEADS, dtype=torch.int32, device=dev)
+    b = batch.c()
+    need = lib.hs2_v1_full_attn_select_workspace_size(ctypes.byref(b), 64, V1_KV_HEADS, 128, top_blocks, HS2_BF16)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check(lib.hs2_v1_full_attn_select(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), q.shape[1],
+                                       k.shape[1] if k.dim() == 3 else V1_KV_HEADS, q.shape[2], top_blocks, scale,
+                                       _ptr(out), _ptr(lse), _ptr(blk_idx), _ptr(blk_count), _ptr(workspace),
+                                       workspace.numel(), _dtype_code(q), _stream(stream)))
+    return out, lse, blk_idx, blk_count
+
+
+def v1_sparse_attn_workspace_size(batch: Batch, top_blocks: int = 16) -> int:
+    b = batch.c()
+    return int(load().hs2_v1_sparse_attn_workspace_size(ctypes.byref(b), 64, V1_KV_HEADS, 128, top_blocks,
+                                                        HS2_BF16))
+
+
+def v1_sparse_attn(batch: Batch, q, k, v, blk_idx, k_swa, v_swa, gate_sparse, gate_swa, window: int = 128,
+                   scale: float | None = None, out=None, workspace=None, stream=None):
+    """hs2_v1_sparse_attn: selected-block branch on the shared cache plus the window branch
+    on the layer's own ring cache k_swa, v_swa [num_seqs, swa_slots, 4, 128], fused by the
+    gates [total_q, 64]. Returns out [total_q, 64, 128]."""
+    lib = load()
+    top_blocks = blk_idx.shape[-1]
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    b = batch.c()
+    need = lib.hs2_v1_sparse_attn_workspace_size(ctypes.byref(b), 64, V1_KV_HEADS, 128, top_blocks, HS2_BF16)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib.hs2_v1_sparse_attn(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), top_blocks,
+                                  _ptr(k_swa), _ptr(v_swa), k_swa.shape[1], window, _ptr(gate_sparse),
+                                  _ptr(gate_swa), q.shape[1], k.shape[1] if k.dim() == 3 else V1_KV_HEADS,
+                                  q.shape[2], scale, _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _dtype_code(q), _stream(stream)))
+    return out

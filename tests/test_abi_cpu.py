@@ -200,3 +200,55 @@ def test_bridge_append_rejects_bad_arguments(lib):
     assert call(rows=FAKE * 6 + 4) == hs2.HS2_ERR_INVALID_ARG  # misaligned
     assert call(cr=-5) == hs2.HS2_ERR_INVALID_ARG
     assert call(ws=ws - 4) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_v1_select_rejects_bad_arguments(lib):
+    b = _batch(total_q=4, max_kv_len=8192, rows=8192)
+    ws = lib.hs2_v1_full_attn_select_workspace_size(ctypes.byref(b), 64, 4, 128, 16, hs2.HS2_BF16)
+    ok_args = dict(nh=64, nkv=4, hd=128, tb=16, scale=0.088, bi=FAKE * 3, ws=ws, dt=hs2.HS2_BF16)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return lib.hs2_v1_full_attn_select(ctypes.byref(b), FAKE, FAKE, FAKE, a["nh"], a["nkv"], a["hd"], a["tb"],
+                                           a["scale"], FAKE * 2, None, a["bi"], None, FAKE, a["ws"], a["dt"], None)
+    assert call(nkv=1) == hs2.HS2_ERR_UNSUPPORTED
+    assert b"n_kv_heads=4" in lib.hs2_last_error()
+    assert call(nh=32) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(dt=hs2.HS2_F32) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(tb=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(tb=65) == hs2.HS2_ERR_INVALID_ARG
+    assert call(scale=0.0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(bi=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(bi=FAKE * 3 + 2) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws=ws - 1) == hs2.HS2_ERR_WORKSPACE
+    big = _batch(total_q=1, max_kv_len=(1 << 21) + 1, rows=(1 << 21) + 1)
+    assert lib.hs2_v1_full_attn_select(ctypes.byref(big), FAKE, FAKE, FAKE, 64, 4, 128, 16, 0.088, FAKE * 2, None,
+                                       FAKE * 3, None, FAKE, 1 << 40, hs2.HS2_BF16, None) == hs2.HS2_ERR_UNSUPPORTED
+    # the workspace holds the partials and the block LSE table, growing with the context
+    b2 = _batch(total_q=4, max_kv_len=4 * 8192, rows=4 * 8192)
+    assert lib.hs2_v1_full_attn_select_workspace_size(ctypes.byref(b2), 64, 4, 128, 16, hs2.HS2_BF16) > ws > 0
+
+
+def test_v1_sparse_rejects_bad_arguments(lib):
+    b = _batch(total_q=4, max_kv_len=8192, rows=8192)
+    ws = lib.hs2_v1_sparse_attn_workspace_size(ctypes.byref(b), 64, 4, 128, 16, hs2.HS2_BF16)
+    assert ws == 4 * 4 * (16 // 2 + 1) * (64 + 16 * 128) * 4
+    ok_args = dict(bi=FAKE * 3, tb=16, ks=FAKE * 4, vs=FAKE * 5, R=128, W=128, gs=FAKE * 6, gw=FAKE * 7, nkv=4,
+                   ws=ws, dt=hs2.HS2_BF16)
+
+    def call(**kw):
+        a = {**ok_args, **kw}
+        return lib.hs2_v1_sparse_attn(ctypes.byref(b), FAKE, FAKE, FAKE, a["bi"], a["tb"], a["ks"], a["vs"], a["R"],
+                                      a["W"], a["gs"], a["gw"], 64, a["nkv"], 128, 0.088, FAKE * 2, FAKE, a["ws"],
+                                      a["dt"], None)
+    assert call(nkv=8) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(dt=hs2.HS2_FP8_E4M3) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(R=64) == hs2.HS2_ERR_INVALID_ARG          # ring shorter than the window
+    assert b"swa_slots" in lib.hs2_last_error()
+    assert call(W=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ks=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(gw=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(gs=FAKE * 6 + 2) == hs2.HS2_ERR_INVALID_ARG
+    assert call(vs=FAKE * 5 + 8) == hs2.HS2_ERR_INVALID_ARG
+    assert call(tb=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws=ws - 1) == hs2.HS2_ERR_WORKSPACE

@@ -1,0 +1,221 @@
+"""GPU parity of the first-generation HySparse layout (GQA 64:4, block selection, gated
+window branch) against the fp64 oracle in oracle/hysparse_v1.py, through the C ABI.
+
+Rules (tests/parity.py): selector outputs max |gpu - fp64| <= 1e-2 and mean <= 1e-3 (bf16
+output of values of magnitude ~1 with fp32 accumulation); LSE within 1e-3. The sparse
+layers' outputs are gated sums of two averages, g1 o_sparse + g2 o_swa with gates up to 1,
+not averages themselves: with few keys they reach |out| ~ 6, where half a bf16 unit is
+2^-6 ~ 1.6e-2 by itself. Their error is therefore taken beyond each element's own output
+rounding, max(0, |gpu - fp64| - ulp_bf16(fp64)/2), with the same max and mean bounds. Block sets: every
+block the oracle keeps with a score above tau (1 + 1e-5) must be kept, none scoring below
+tau (1 - 1e-5) may be, the count is min(top_blocks, t/64 + 1), the list is ascending and
+padded with -1 (tau = the oracle's kept score of rank top_blocks). The sparse layers are
+checked against the oracle run on the GPU's own block sets, so a block swapped inside the
+tolerance band does not count twice.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hysparse_v1 as ov1
+from tests.parity import MAX_ABS, MEAN_ABS, check_attn, check_lse, from_dev, half_ulp_bf16, to_dev
+from workloads.gen import stored_to_f64
+from workloads.v1 import kv_rows, make_v1_inputs, v1_config
+
+pytestmark = pytest.mark.gpu
+
+REL_BAND = 1e-5
+
+
+def _hs2():
+    from long_context_mqa_amd import hs2
+    return hs2
+
+
+def _batch(inp):
+    hs2 = _hs2()
+    return hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, inp.spec.total_rows)
+
+
+def _kv_f64(inp, qi):
+    s = int(inp.q_seq[qi])
+    a = int(inp.kv_start[s])
+    t = int(inp.q_pos[qi])
+    return stored_to_f64(kv_rows(inp, "k", a, a + t + 1)), stored_to_f64(kv_rows(inp, "v", a, a + t + 1)), t
+
+
+def _swa_f64(inp, layer, qi):
+    """The window ring of the query's sequence as a position-indexed array (rows outside
+    the window stay zero; the oracle reads only the window)."""
+    s = int(inp.q_seq[qi])
+    t = int(inp.q_pos[qi])
+    R = inp.k_swa[layer].shape[1]
+    K = np.zeros((t + 1, 4, 128))
+    V = np.zeros((t + 1, 4, 128))
+    for p in range(max(0, t - inp.spec.window + 1), t + 1):
+        K[p] = stored_to_f64(inp.k_swa[layer][s, p % R])
+        V[p] = stored_to_f64(inp.v_swa[layer][s, p % R])
+    return K, V
+
+
+def check_gated(gpu: np.ndarray, ref: np.ndarray, what: str):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    e = np.maximum(0.0, np.abs(gpu - ref) - half_ulp_bf16(ref))
+    assert e.max() <= MAX_ABS, f"{what}: max abs err beyond rounding {e.max():.3e}"
+    assert e.mean() <= MEAN_ABS, f"{what}: mean abs err beyond rounding {e.mean():.3e}"
+
+
+def check_blocks(gpu_idx, gpu_cnt, ref, t, top_blocks, what):
+    nblk = t // 64 + 1
+    for g in range(4):
+        k_eff = min(top_blocks, nblk)
+        assert int(gpu_cnt[g]) == k_eff, f"{what} g{g}: count {gpu_cnt[g]} != {k_eff}"
+        sel = np.asarray(gpu_idx[g][:k_eff], dtype=np.int64)
+        assert np.all(np.asarray(gpu_idx[g][k_eff:]) == -1), f"{what} g{g}: padding is not -1"
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < nblk, f"{what} g{g}: bad list {sel}"
+        tau = ref["tau"][g]
+        if tau is None:
+            assert sel.tolist() == ref["sel"][g].tolist(), f"{what} g{g}: all blocks expected"
+            continue
+        sc = ref["scores"][g]
+        must = ref["sel"][g][sc[ref["sel"][g]] > tau * (1 + REL_BAND)]
+        missing = np.setdiff1d(must, sel)
+        assert missing.size == 0, f"{what} g{g}: clearly-kept blocks missing {missing}"
+        bad = sel[sc[sel] < tau * (1 - REL_BAND)]
+        assert bad.size == 0, f"{what} g{g}: clearly-dropped blocks kept {bad}"
+
+
+def run_v1(inp, k_dev=None, v_dev=None):
+    hs2 = _hs2()
+    b = _batch(inp)
+    k = to_dev(inp.k) if k_dev is None else k_dev
+    v = to_dev(inp.v) if v_dev is None else v_dev
+    out, lse, bi, bc = hs2.v1_full_attn_select(b, to_dev(inp.q_sel), k, v, top_blocks=inp.spec.top_blocks)
+    sp = []
+    for l in range(inp.spec.n_sparse):
+        sp.append(hs2.v1_sparse_attn(b, to_dev(inp.q_sp[l]), k, v, bi, to_dev(inp.k_swa[l]), to_dev(inp.v_swa[l]),
+                                     to_dev(inp.gate_sp[l]), to_dev(inp.gate_swa[l]), window=inp.spec.window))
+    torch.cuda.synchronize()
+    return (from_dev(out), lse.cpu().numpy().astype(np.float64), bi.cpu().numpy(), bc.cpu().numpy(),
+            [from_dev(x) for x in sp])
+
+
+def check_queries(inp, res, queries, what):
+    out, lse, bi, bc, sp = res
+    sc = inp.spec
+    for qi in queries:
+        K, V, t = _kv_f64(inp, qi)
+        q = stored_to_f64(inp.q_sel[qi])
+        ref = ov1.v1_selector_query(q, K, V, t, sc.scale, sc.top_blocks)
+        tag = f"{what} q{qi} t={t}"
+        check_attn(out[qi], ref["out"], tag)
+        check_lse(lse[qi], ref["lse"], tag)
+        check_blocks(bi[qi], bc[qi], ref, t, sc.top_blocks, tag)
+        for l in range(sc.n_sparse):
+            Ks, Vs = _swa_f64(inp, l, qi)
+            blocks = [bi[qi][g][: bc[qi][g]] for g in range(4)]
+            o, _, _ = ov1.v1_sparse_query(stored_to_f64(inp.q_sp[l][qi]), K, V, t, blocks, Ks, Vs,
+                                          inp.gate_sp[l][qi].astype(np.float64),
+                                          inp.gate_swa[l][qi].astype(np.float64), sc.scale, sc.window)
+            check_gated(sp[l][qi], o, f"{tag} sparse layer {l}")
+
+
+def test_v1_small_ragged_block():
+    """Short and ragged sequences: partial blocks, t = 0, fewer blocks than top_blocks,
+    several queries per sequence, selector parts split over many workgroups."""
+    inp = make_v1_inputs(v1_config(10))
+    res = run_v1(inp)
+    check_queries(inp, res, range(inp.spec.total_q), "small")
+    # planted needles: the needle's block is kept for its KV head
+    _, _, bi, bc, _ = res
+    row_q = {}
+    for qi in range(inp.spec.total_q):
+        row_q.setdefault(int(inp.q_seq[qi]), []).append(qi)
+    for row, g, _ in inp.needles:
+        s = int(np.searchsorted(inp.kv_start, row, side="right") - 1)
+        blk = (row - int(inp.kv_start[s])) // 64
+        hit = [blk in bi[qi][g][: bc[qi][g]].tolist() for qi in row_q[s]]
+        assert any(hit), f"needle at row {row} (KV head {g}) not kept by any query of sequence {s}"
+
+
+def test_v1_top_blocks_and_gate_edges():
+    """top_blocks 1 and 64, zero gates on either branch, and a block list with padding,
+    out-of-range entries and an empty KV head (only the window branch contributes)."""
+    hs2 = _hs2()
+    spec = v1_config(10, n_sparse=1)
+    inp = make_v1_inputs(spec)
+    b = _batch(inp)
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    q = to_dev(inp.q_sel)
+    for tb in (1, 64):
+        out, lse, bi, bc = hs2.v1_full_attn_select(b, q, k, v, top_blocks=tb)
+        torch.cuda.synchronize()
+        for qi in range(spec.total_q):
+            K, V, t = _kv_f64(inp, qi)
+            ref = ov1.v1_selector_query(stored_to_f64(inp.q_sel[qi]), K, V, t, spec.scale, tb)
+            check_attn(from_dev(out[qi]), ref["out"], f"tb={tb} q{qi}")
+            check_blocks(bi[qi].cpu().numpy(), bc[qi].cpu().numpy(), ref, t, tb, f"tb={tb} q{qi}")
+    # hand-made block lists: padding, an entry beyond t/64, an empty KV head
+    nq = spec.total_q
+    blk = np.full((nq, 4, 16), -1, dtype=np.int32)
+    for qi in range(nq):
+        t = int(inp.q_pos[qi])
+        nb = t // 64 + 1
+        blk[qi, 0, :3] = [0, nb - 1, nb + 5] if nb > 1 else [0, -1, nb + 5]
+        blk[qi, 1, :2] = [nb // 2, 10**6]
+        blk[qi, 3, 0] = nb - 1
+    bl = torch.from_numpy(blk).cuda()
+    ks, vs = to_dev(inp.k_swa[0]), to_dev(inp.v_swa[0])
+    for gs_val, gw_val in ((1.0, 0.0), (0.0, 1.0), (None, None)):
+        gsp = inp.gate_sp[0] if gs_val is None else np.full((nq, 64), gs_val, np.float32)
+        gsw = inp.gate_swa[0] if gw_val is None else np.full((nq, 64), gw_val, np.float32)
+        o = hs2.v1_sparse_attn(b, to_dev(inp.q_sp[0]), k, v, bl, ks, vs, to_dev(gsp), to_dev(gsw),
+                               window=spec.window)
+        torch.cuda.synchronize()
+        o = from_dev(o)
+        for qi in range(nq):
+            K, V, t = _kv_f64(inp, qi)
+            Ks, Vs = _swa_f64(inp, 0, qi)
+            blocks = [blk[qi, g][(blk[qi, g] >= 0) & (blk[qi, g] <= t // 64)] for g in range(4)]
+            ref, _, _ = ov1.v1_sparse_query(stored_to_f64(inp.q_sp[0][qi]), K, V, t, blocks, Ks, Vs,
+                                            gsp[qi].astype(np.float64), gsw[qi].astype(np.float64), spec.scale,
+                                            spec.window)
+            check_gated(o[qi], ref, f"gates {gs_val},{gw_val} q{qi}")
+
+
+def test_v1_invalid_descriptor_gives_nan():
+    hs2 = _hs2()
+    spec = v1_config(10, n_sparse=1)
+    inp = make_v1_inputs(spec)
+    qp = inp.q_pos.copy()
+    qp[3] = int(inp.kv_len[0]) + 7          # beyond its sequence
+    b = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, qp, spec.total_rows)
+    out, lse, bi, bc = hs2.v1_full_attn_select(b, to_dev(inp.q_sel), to_dev(inp.k), to_dev(inp.v))
+    o = hs2.v1_sparse_attn(b, to_dev(inp.q_sp[0]), to_dev(inp.k), to_dev(inp.v), bi, to_dev(inp.k_swa[0]),
+                           to_dev(inp.v_swa[0]), to_dev(inp.gate_sp[0]), to_dev(inp.gate_swa[0]))
+    torch.cuda.synchronize()
+    assert torch.isnan(out[3].float()).all() and torch.isnan(lse[3]).all() and torch.isnan(o[3].float()).all()
+    assert (bc[3] == -1).all() and (bi[3] == -1).all()
+    assert torch.isfinite(out[2].float()).all() and (bc[2] > 0).all()
+
+
+def test_v1_decode_64x128k_sampled():
+    """The 64 x 131,072-token decode batch in the launch configuration of the benchmark,
+    checked on two sampled queries. The sampled sequences hold the workload's exact rows;
+    the other sequences hold seeded device-side N(0,1) rows of the same shape (their
+    queries are computed but not compared)."""
+    hs2 = _hs2()
+    spec = v1_config(9)
+    inp = make_v1_inputs(spec, with_kv=False)
+    rows = spec.total_rows
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    k = torch.randn(rows, 4, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(rows, 4, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    sample = [5, 58]
+    for qi in sample:
+        s = int(inp.q_seq[qi])
+        a, n = int(inp.kv_start[s]), int(inp.kv_len[s])
+        k[a:a + n] = to_dev(kv_rows(inp, "k", a, a + n))
+        v[a:a + n] = to_dev(kv_rows(inp, "v", a, a + n))
+    res = run_v1(inp, k, v)
+    check_queries(inp, res, sample, "decode-64x128k")

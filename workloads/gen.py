@@ -41,6 +41,32 @@ def normal_f32(seed: int, tag: int, n: int, std: float = 1.0) -> np.ndarray:
     return out
 
 
+def normal_f32_range(seed: int, tag: int, lo: int, hi: int, std: float = 1.0) -> np.ndarray:
+    """Elements lo .. hi-1 of normal_f32(seed, tag, n, std), for any n >= hi: each chunk's
+    stream is drawn from its start, and a shorter draw is a prefix of a longer one."""
+    out = np.empty(max(0, hi - lo), dtype=np.float32)
+    if hi <= lo:
+        return out
+
+    def fill(c: int) -> None:
+        a = max(lo, c * CHUNK)
+        b = min(hi, (c + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, c])))
+        buf = g.standard_normal(b - c * CHUNK, dtype=np.float32)
+        out[a - lo:b - lo] = buf[a - c * CHUNK:]
+        if std != 1.0:
+            out[a - lo:b - lo] *= np.float32(std)
+
+    chunks = range(lo // CHUNK, (hi - 1) // CHUNK + 1)
+    if len(chunks) <= 1:
+        for c in chunks:
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, chunks))
+    return out
+
+
 def rng(seed: int, tag: int) -> np.random.Generator:
     """A small-draw generator (positions, lengths) for one purpose of one seed."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, 1 << 30])))
