@@ -12,6 +12,9 @@ default workload with the decode-time KV Bridging of the 64 new tokens into 3 la
 caches ahead of the selector; `--workload 7` is a
 prefill: KV Bridging of 262,144 hidden states, then exact causal attention of every one of
 the 262,144 positions (the self-decoder's full-attention layer, no selection).
+`--workload 9` is the first-generation HySparse layout (the comparison variant) on the
+default decode batch: GQA 64:4 selector with 64-token block selection, then 7 sparse
+layers that fuse the selected blocks with a 128-token window branch through gates.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events recorded by the
 library around each kernel it launches, on the stream it launches on.
@@ -49,7 +52,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8, 9])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -149,6 +152,8 @@ def main() -> int:
     hs2.load()
     if args.workload == 7:
         return run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs)
+    if args.workload == 9:
+        return run_v1(args, hs2)
     append = args.workload == 8
     spec = block_config(2 if append else args.workload)
     log(f"generating {spec.name}")
@@ -479,6 +484,160 @@ def run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs) 
         "bridging": {"ms": gemm_ms, "tflops": f_br / (gemm_ms * 1e-3) / 1e12,
                      "frac_mfma": f_br / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline_v1(inp, budget_s: float):
+    """The fp64 first-generation oracle, unchanged, on a bounded sample of the queries."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import hysparse_v1 as ov1
+    from workloads.gen import stored_to_f64
+    from workloads.v1 import kv_rows
+
+    sp = inp.spec
+    order = list(range(sp.total_q))
+    np.random.default_rng(0).shuffle(order)
+    done, spent = 0, 0.0
+    for qi in order:
+        s = int(inp.q_seq[qi])
+        a, t = int(inp.kv_start[s]), int(inp.q_pos[qi])
+        K = stored_to_f64(kv_rows(inp, "k", a, a + t + 1))
+        V = stored_to_f64(kv_rows(inp, "v", a, a + t + 1))
+        R = inp.k_swa[0].shape[1]
+        swa = []
+        for l in range(sp.n_sparse):
+            Ks = np.zeros((t + 1, 4, 128))
+            Vs = np.zeros((t + 1, 4, 128))
+            for p_ in range(max(0, t - sp.window + 1), t + 1):
+                Ks[p_] = stored_to_f64(inp.k_swa[l][s, p_ % R])
+                Vs[p_] = stored_to_f64(inp.v_swa[l][s, p_ % R])
+            swa.append((Ks, Vs))
+        q = stored_to_f64(inp.q_sel[qi])
+        qs = [stored_to_f64(x[qi]) for x in inp.q_sp]
+        t0 = time.perf_counter()
+        r = ov1.v1_selector_query(q, K, V, t, sp.scale, sp.top_blocks)
+        for l in range(sp.n_sparse):
+            ov1.v1_sparse_query(qs[l], K, V, t, r["sel"], swa[l][0], swa[l][1], inp.gate_sp[l][qi].astype(np.float64),
+                                inp.gate_swa[l][qi].astype(np.float64), sp.scale, sp.window)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {sp.total_q} queries of {sp.name} (selector + {sp.n_sparse} sparse layers "
+                      f"each, fp64, {spent:.1f} s)"}
+
+
+def run_v1(args, hs2) -> int:
+    """Workload 9: the first-generation layout on the decode batch of workload 2. A step is
+    the GQA selector (exact attention plus block selection) and 7 gated sparse layers."""
+    import numpy as np
+    import torch
+
+    from workloads.v1 import kv_rows, make_v1_inputs, v1_config
+
+    spec = v1_config(9)
+    log(f"generating {spec.name}")
+    inp = make_v1_inputs(spec, with_kv=False)
+    dev = torch.device("cuda:0")
+    rows = spec.total_rows
+    k = torch.empty(rows, 4, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(rows, 4, 128, dtype=torch.bfloat16, device=dev)
+    for si in range(len(spec.seq_lens)):   # one sequence at a time: no whole host copy
+        a, n = int(inp.kv_start[si]), int(inp.kv_len[si])
+        k[a:a + n] = to_dev(kv_rows(inp, "k", a, a + n))
+        v[a:a + n] = to_dev(kv_rows(inp, "v", a, a + n))
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, rows, dev)
+    q_sel = to_dev(inp.q_sel)
+    q_sp = [to_dev(x) for x in inp.q_sp]
+    k_swa = [to_dev(x) for x in inp.k_swa]
+    v_swa = [to_dev(x) for x in inp.v_swa]
+    g_sp = [to_dev(x) for x in inp.gate_sp]
+    g_sw = [to_dev(x) for x in inp.gate_swa]
+    nq = spec.total_q
+    out = torch.empty_like(q_sel)
+    lse = torch.empty(nq, 64, dtype=torch.float32, device=dev)
+    bi = torch.empty(nq, 4, spec.top_blocks, dtype=torch.int32, device=dev)
+    bc = torch.empty(nq, 4, dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(hs2.v1_full_attn_select_workspace_size(batch, spec.top_blocks), dtype=torch.uint8, device=dev)
+    ws_sp = torch.empty(hs2.v1_sparse_attn_workspace_size(batch, spec.top_blocks), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q_sel) for _ in range(spec.n_sparse)]
+    torch.cuda.synchronize()
+
+    def new_events(m):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(m)]
+        for e in evs:
+            e.record(torch.cuda.current_stream())
+        return evs
+
+    def step(ev_sel=None, ev_sp=None):
+        hs2.set_kernel_events([e.cuda_event for e in ev_sel] if ev_sel else None)
+        hs2.v1_full_attn_select(batch, q_sel, k, v, spec.top_blocks, spec.scale, out=out, lse=lse, blk_idx=bi,
+                                blk_count=bc, workspace=ws_sel)
+        for l in range(spec.n_sparse):
+            hs2.set_kernel_events([e.cuda_event for e in ev_sp[l]] if ev_sp else None)
+            hs2.v1_sparse_attn(batch, q_sp[l], k, v, bi, k_swa[l], v_swa[l], g_sp[l], g_sw[l], spec.window,
+                               spec.scale, out=outs[l], workspace=ws_sp)
+        hs2.set_kernel_events(None)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [new_events(2) for _ in range(args.steps)]   # selector attention pass only
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    att_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # one instrumented step after the timed ones: every kernel of the step
+    ev_all = new_events(4)
+    ev_l = [new_events(4) for _ in range(spec.n_sparse)]
+    torch.cuda.synchronize()
+    step(ev_all, ev_l)
+    torch.cuda.synchronize()
+    kms = {"v1_attn_pass": ev_all[0].elapsed_time(ev_all[1]), "v1_combine_select": ev_all[2].elapsed_time(ev_all[3]),
+           "v1_sparse_attn": float(np.mean([e[0].elapsed_time(e[1]) for e in ev_l])),
+           "v1_gate_combine": float(np.mean([e[2].elapsed_time(e[3]) for e in ev_l]))}
+    keys = int(np.sum(inp.q_pos.astype(np.int64) + 1))
+    alg = keys * 4 * 128 * 2 * 2 + nq * 64 * 128 * 2       # K and V of every key (4 KV heads), plus Q
+    ach = alg / (att_ms * 1e-3) / 1e9
+    sp_keys = nq * 4 * (spec.top_blocks * 64 + spec.window)
+    sp_bytes = sp_keys * 2 * 128 * 2 + nq * 64 * 128 * 2
+    res = {
+        "metric": METRIC,
+        "value": nq / (elapsed / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V and window K/V (bf16), uniform [0,1) gates, 8 needles per query",
+        "config": {"workload": spec.name, "seqs": len(spec.seq_lens), "ctx": spec.seq_lens[0], "queries": nq,
+                   "q_heads": 64, "kv_heads": 4, "head_dim": 128, "block": 64, "top_blocks": spec.top_blocks,
+                   "window": spec.window, "layers": {"selector": 1, "sparse": spec.n_sparse},
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "v1_attn_pass (GQA selector attention with block LSEs)", "bound": "hbm",
+                     "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": None, "alg_bytes_per_launch": alg, "avg_launch_ms": att_ms},
+        "kernels_ms": kms,
+        "kernels_ms_source": "roofline kernel: HIP events inside the timed steps; others: one instrumented step",
+        "sparse_layer": {"alg_bytes": sp_bytes, "us": kms["v1_sparse_attn"] * 1e3,
+                         "gbps": sp_bytes / (kms["v1_sparse_attn"] * 1e-3) / 1e9},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_v1(inp, args.cpu_seconds),
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -1,7 +1,9 @@
 /*
  * hs2.h -- C ABI of the HySparse2 attention hot path on AMD Instinct MI355X (gfx950).
  *
- * Three operations, with one KV head shared by 64 query heads (MQA):
+ * The HySparse2 operations, with one KV head shared by 64 query heads (MQA), and at the
+ * end the first-generation layout (GQA 64:4, block selection, gated window branch) as a
+ * comparison variant (hs2_v1_*):
  *   hs2_bridge_kv         KV Bridging: one read of the self-decoder hidden states is
  *                         projected through separate K/V weights for several layers.
  *   hs2_full_attn_select  the cross-decoder full-attention (selector) layer: exact
