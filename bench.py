@@ -62,7 +62,7 @@ def parse():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "attn_common.h", "hs2_internal.h"):
+    for f in ("attn_decode.h", "attn_common.h", "hs2_internal.h"):
         with open(os.path.join(ROOT, "long_context_mqa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -18,12 +18,12 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhs2.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "attn_chunk.hip", "score_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "bridge_append.hip", "attn_v1.hip",
+SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_chunk.hip", "score_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "bridge_append.hip", "attn_v1.hip",
            "hs2_api.cpp"]
 # Kernels whose MFMA results are consumed element by element every tile and that fit in
 # the 256 VGPRs: MFMA destinations in VGPRs instead of accumulator registers (AGPRs),
 # which saves a v_accvgpr_read per result element.
-VGPR_MFMA = {"attn_chunk.hip", "score_bf16.hip"}
+VGPR_MFMA = {"attn_chunk.hip", "score_bf16.hip", "attn_fp8.hip"}
 
 
 def hipcc() -> str:

@@ -56,7 +56,7 @@ struct AttnArgs {
   int32_t top_k;
   float c2;               // softmax scale * log2(e)
   int32_t n_split;        // workgroups per query
-  int32_t split_keys;     // logical keys per workgroup (multiple of kTile * kWaves)
+  int32_t split_keys;     // logical keys per workgroup (multiple of kTile)
   Partial* part;          // [total_q][n_split] when n_split > 1
   void* out;              // [total_q][64][128] when n_split == 1
   float* lse;             // [total_q][64] natural log, nullable (n_split == 1)
