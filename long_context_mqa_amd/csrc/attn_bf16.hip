@@ -40,17 +40,29 @@ using namespace attn;
 // ------------------------------------------------------------------------------------
 // Split combine: merges the partials of a query in split order, writes O, LSE and the
 // log2-domain LSE used by the score pass, and clears the query's selection counters.
-// Grid: total_q x kCombineSlabs; a slab covers 16 dims x 64 heads of the output.
+// Grid: total_q x kCombineSlabs; a slab covers 16 dims x 64 heads of the output. Thread
+// (h, g) merges head h's partials for 4 dims on its own (online, with a running
+// reference, in split order), so that the loads of several splits are in flight at once
+// and no barrier separates them; every thread of a head computes the same denominators.
 // ------------------------------------------------------------------------------------
 constexpr int kCombineSlabs = kDim / 16;
-constexpr int kMaxSplit = 256;
+
+struct MergeAcc {
+  float m = -INFINITY, l = 0.0f, le = 0.0f;
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  __device__ inline void add(float ms, float ls, float les, const float (&os)[4]) {
+    const float mn = fmaxf(m, ms);
+    const float fa = __builtin_amdgcn_exp2f(m - mn), fb = __builtin_amdgcn_exp2f(ms - mn);
+    l = l * fa + ls * fb;
+    le = le * fa + les * fb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = o[r] * fa + os[r] * fb;
+    m = mn;
+  }
+};
 
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ float w_s[kMaxSplit][kHeads];
-  __shared__ float red[4][kHeads];
-  __shared__ float rede[4][kHeads];
-  __shared__ float fm[kHeads], fl[kHeads];
   const int i = blockIdx.x / kCombineSlabs;
   const int slab = blockIdx.x - i * kCombineSlabs;
   const int tid = threadIdx.x;
@@ -77,59 +89,35 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int n_keys = logical_keys(a.gather != 0, t, a.window, a.top_k);
   const int nv = min(a.n_split, (n_keys + a.split_keys - 1) / a.split_keys);
   const Partial* P = a.part + (size_t)i * a.n_split;
-  // max over splits: four groups of 64 threads take every fourth split
-  float mx = -INFINITY;
-  for (int s2 = grp; s2 < nv; s2 += 4) mx = fmaxf(mx, P[s2].m[h]);
-  red[grp][h] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-  __syncthreads();
-  float lsum = 0.0f, esum = 0.0f;
-  for (int s2 = grp; s2 < nv; s2 += 4) {
-    const float w = __builtin_amdgcn_exp2f(P[s2].m[h] - M);
-    w_s[s2][h] = w;
-    lsum += P[s2].l[h] * w;
-    esum += P[s2].le[h] * w;
-  }
-  red[grp][h] = lsum;
-  rede[grp][h] = esum;
-  __syncthreads();
-  if (tid < kHeads) {
-    const float L = (red[0][h] + red[1][h]) + (red[2][h] + red[3][h]);
-    const float LE = (rede[0][h] + rede[1][h]) + (rede[2][h] + rede[3][h]);
-    fm[h] = M;
-    fl[h] = L;
-    if (slab == 0) {
-      const float l2 = M + __log2f(LE);
-      if (a.lse) a.lse[(size_t)i * kHeads + h] = l2 * kLn2;
-      if (a.lse2) a.lse2[(size_t)i * kHeads + h] = l2;
-    }
-  }
-  __syncthreads();
-  // thread (h, grp): dims d0 .. d0+3 of head h; loads of 4 splits in flight at a time
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  MergeAcc acc;
   int s2 = 0;
   for (; s2 + 4 <= nv; s2 += 4) {
-    float v[4][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[u][r] = P[s2 + u].o[(d0 + r) * kHeads + h];
+    float m[4], l[4], le[4], v[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = w_s[s2 + u][h];
+      m[u] = P[s2 + u].m[h];
+      l[u] = P[s2 + u].l[h];
+      le[u] = P[s2 + u].le[h];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += v[u][r] * w;
+      for (int r = 0; r < 4; ++r) v[u][r] = P[s2 + u].o[(d0 + r) * kHeads + h];
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc.add(m[u], l[u], le[u], v[u]);
   }
   for (; s2 < nv; ++s2) {
-    const float w = w_s[s2][h];
+    float v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += P[s2].o[(d0 + r) * kHeads + h] * w;
+    for (int r = 0; r < 4; ++r) v[r] = P[s2].o[(d0 + r) * kHeads + h];
+    acc.add(P[s2].m[h], P[s2].l[h], P[s2].le[h], v);
   }
-  const float inv = a.v_scale / fl[h];
+  if (slab == 0 && grp == 0) {
+    const float l2 = acc.m + __log2f(acc.le);
+    if (a.lse) a.lse[(size_t)i * kHeads + h] = l2 * kLn2;
+    if (a.lse2) a.lse2[(size_t)i * kHeads + h] = l2;
+  }
+  const float inv = a.v_scale / acc.l;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)(acc[r] * inv);
+  for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)(acc.o[r] * inv);
 }
 
 }  // namespace
