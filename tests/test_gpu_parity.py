@@ -188,6 +188,29 @@ def test_window_and_k_small():
     check_all_queries_properties(inp, g)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_largest_top_k(dtype):
+    """top_k at its bound (HS2_MAX_TOP_K = 4096): the selection and the sparse layer's
+    4,224-key gather (several sparse splits of up to 2,048 slots)."""
+    spec = BlockSpec(f"k4096-{dtype}", [65536, 20000], [[65535, 40000], [19999]], dtype=dtype, n_sparse=1,
+                     needles_per_query=8, seed=21, top_k=4096)
+    inp = make_block_inputs(spec)
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), f"k4096-{dtype}")
+    check_all_queries_properties(inp, g)
+
+
+def test_largest_window():
+    """window at its bound (2^18 = 262,144) over a 300,000-token context: 37,856 and 17,857
+    candidates, and a sparse layer of 263,168 keys per query."""
+    spec = BlockSpec("w2^18", [300000], [[299999, 280000]], dtype="bf16", n_sparse=1, needles_per_query=4,
+                     seed=22, window=1 << 18, top_k=1024)
+    inp = make_block_inputs(spec)
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), "w2^18")
+    check_all_queries_properties(inp, g)
+
+
 def test_exact_ties_prefer_smaller_position():
     """Identical key rows give bitwise-equal scores; the k-th place must go to the
     smallest positions among them."""
