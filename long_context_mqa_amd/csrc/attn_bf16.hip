@@ -131,6 +131,16 @@ hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, 
   return hipGetLastError();
 }
 
+hipError_t launch_attn_fp8kv_full(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist,
+                                  uint32_t* counters, hipStream_t s);  // attn_fp8.hip
+
+hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
+                             uint32_t* counters, hipStream_t s) {
+  if (!gather) return launch_attn_fp8kv_full(a, wl, grid, hist, counters, s);
+  hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, true, 4>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s) {
   const dim3 grid(a.b.total_q * kCombineSlabs);
   if (f32)
