@@ -136,51 +136,29 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
 
   const int KT = a.d_model / kKStep;  // >= 1 (d_model is a multiple of 64)
   static_assert(kStagesG == 2, "the loop below keeps one stage in flight");
-  // operands of contraction step ks of the stage in LDS buffer st
-  auto read_ops = [&](int st, int ks, bf16x8 (&av)[kXB], bf16x8 (&bv)[2]) {
-    const int c = 2 * ks + (lane >> 5);
-#pragma unroll
-    for (int x = 0; x < kXB; ++x)
-      av[x] = *reinterpret_cast<const bf16x8*>(lds_a[st] + op_off(wc * (kCols / 2) + 32 * x + (lane & 31), c));
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-      bv[y] = *reinterpret_cast<const bf16x8*>(lds_b[st] + op_off(wr * 64 + 32 * y + (lane & 31), c));
-  };
-  // the products of one stage; the operands of its first step are already in av, bv
-  auto stage_products = [&](int st, bf16x8 (&av)[kXB], bf16x8 (&bv)[2]) {
+  issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % kStagesG;
+    wait_vm<0>();  // this wave's copies of stage kt have landed (the only ones in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // the whole stage has landed; stage kt-1 is no longer read
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) % kStagesG);
 #pragma unroll
     for (int ks = 0; ks < kKStep / 16; ++ks) {
-      if (ks > 0) read_ops(st, ks, av, bv);
+      const int c = 2 * ks + (lane >> 5);
+      bf16x8 av[kXB], bv[2];
+#pragma unroll
+      for (int x = 0; x < kXB; ++x)
+        av[x] = *reinterpret_cast<const bf16x8*>(lds_a[st] + op_off(wc * (kCols / 2) + 32 * x + (lane & 31), c));
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        bv[y] = *reinterpret_cast<const bf16x8*>(lds_b[st] + op_off(wr * 64 + 32 * y + (lane & 31), c));
 #pragma unroll
       for (int x = 0; x < kXB; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
-  };
-  auto stage_ready = [&]() {
-    wait_vm<0>();  // this wave's copies of the stage have landed (the only ones in flight)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // the whole stage has landed; the other buffer is no longer read
-  };
-  issue(0, 0);
-  // Steady state without a branch, so that the copies of stage kt+1 and the products of
-  // stage kt share one basic block: the first step's operands are read before the copies
-  // are issued (they go to the other buffer) and its products can run under the issue.
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    const int st = kt % kStagesG;
-    stage_ready();
-    bf16x8 av[kXB], bv[2];
-    read_ops(st, 0, av, bv);
-    issue(kt + 1, (kt + 1) % kStagesG);
-    stage_products(st, av, bv);
-  }
-  {
-    const int st = (KT - 1) % kStagesG;
-    stage_ready();
-    bf16x8 av[kXB], bv[2];
-    read_ops(st, 0, av, bv);
-    stage_products(st, av, bv);
   }
 
   // C^T[n][row]: lane holds rows 32*y + l%32, columns 32*x + 8*(j/4) + 4*(l/32) + j%4
