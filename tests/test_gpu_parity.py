@@ -248,8 +248,9 @@ def test_invalid_descriptor_is_not_computed():
     check_selection(g["sel"][0], int(g["count"][0]), r, spec.top_k, 3000 - 127, "valid neighbour")
 
 
-def test_repeat_runs_are_bitwise_identical():
-    inp = make_block_inputs(BlockSpec("det", [20000, 7000], [[19999], [6999, 3000]], dtype="bf16", n_sparse=1,
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_repeat_runs_are_bitwise_identical(dtype):
+    inp = make_block_inputs(BlockSpec("det", [20000, 7000], [[19999], [6999, 3000]], dtype=dtype, n_sparse=1,
                                       needles_per_query=4, seed=18))
     a = run_block(inp)
     b = run_block(inp)

@@ -219,3 +219,31 @@ def test_v1_decode_64x128k_sampled():
         v[a:a + n] = to_dev(kv_rows(inp, "v", a, a + n))
     res = run_v1(inp, k, v)
     check_queries(inp, res, sample, "decode-64x128k")
+
+
+def test_v1_repeat_runs_bitwise_and_workspace_contents_do_not_matter():
+    """Two runs give bitwise-equal outputs and block sets, and the workspaces (split
+    partials and the block LSE table) may hold arbitrary bytes on entry (0xFF bytes read
+    as NaN floats, 0x00, 0x01) or the previous call's contents."""
+    hs2 = _hs2()
+    spec = v1_config(10, n_sparse=1)
+    inp = make_v1_inputs(spec)
+    b = _batch(inp)
+    k, v, q, qs = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel), to_dev(inp.q_sp[0])
+    ks, vs = to_dev(inp.k_swa[0]), to_dev(inp.v_swa[0])
+    gsp, gsw = to_dev(inp.gate_sp[0]), to_dev(inp.gate_swa[0])
+    ws_sel = torch.empty(hs2.v1_full_attn_select_workspace_size(b, spec.top_blocks), dtype=torch.uint8, device="cuda")
+    ws_sp = torch.empty(hs2.v1_sparse_attn_workspace_size(b, spec.top_blocks), dtype=torch.uint8, device="cuda")
+    results = []
+    for fill in (0xFF, 0x00, 0x01, None, None):
+        if fill is not None:
+            ws_sel.fill_(fill)
+            ws_sp.fill_(fill)
+        out, lse, bi, bc = hs2.v1_full_attn_select(b, q, k, v, top_blocks=spec.top_blocks, workspace=ws_sel)
+        o = hs2.v1_sparse_attn(b, qs, k, v, bi, ks, vs, gsp, gsw, window=spec.window, workspace=ws_sp)
+        torch.cuda.synchronize()
+        results.append([x.cpu().clone() for x in (out, lse, bi, bc, o)])
+    for r in results[1:]:
+        for x, y in zip(results[0], r):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
