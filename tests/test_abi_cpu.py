@@ -252,3 +252,33 @@ def test_v1_sparse_rejects_bad_arguments(lib):
     assert call(vs=FAKE * 5 + 8) == hs2.HS2_ERR_INVALID_ARG
     assert call(tb=0) == hs2.HS2_ERR_INVALID_ARG
     assert call(ws=ws - 1) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_header_is_plain_c99_and_a_c_program_links(lib, tmp_path):
+    """include/hs2.h compiles as strict C99 (no C++ or compiler extensions needed) and a
+    C program links against libhs2.so and calls it (host-only calls: no GPU needed)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "t.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "hs2.h"\n'
+        "int main(void) {\n"
+        "  hs2_seqs b = {0};\n"
+        "  if (hs2_version() != HS2_VERSION) return 1;\n"
+        "  if (hs2_full_attn_select(&b, 0, 0, 0, 64, 128, 128, 1024, 0.1f, 0, 0, 0, 0, 0, 0, HS2_BF16, 0)\n"
+        "      != HS2_ERR_INVALID_ARG) return 2;\n"
+        '  printf("%s\\n", hs2_last_error());\n'
+        "  return 0;\n}\n")
+    exe = tmp_path / "t"
+    lib_dir = os.path.dirname(hs2.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-L", lib_dir, "-lhs2", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "num_seqs" in r.stdout
