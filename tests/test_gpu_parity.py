@@ -543,3 +543,63 @@ def test_logit_far_above_first_tile_is_recomputed(shape):
     g = run_block(inp)
     check_queries(inp, g, range(spec.total_q), f"spike-{shape}")
     assert int(pos[int(np.argmax(xs))]) in set(g["sel"][qi].tolist())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_step_replays_from_a_hip_graph(dtype):
+    """The entry points launch kernels only (no allocation, memset, copy or synchronisation),
+    so a caller can capture a decode step (selector + a sparse layer) into a HIP graph.
+    Each replay is checked against the eager run, with eager work on the outputs between
+    replays."""
+    spec = BlockSpec(f"graph-{dtype}", [30000, 9000], [[29999], [8999]], dtype=dtype, n_sparse=1,
+                     needles_per_query=2, seed=33)
+    inp = make_block_inputs(spec)
+    dev = "cuda"
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, dev)
+    k, v, q, qs = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel), to_dev(inp.q_sp[0])
+    nq = spec.total_q
+    out = torch.empty_like(q)
+    lse = torch.empty(nq, 64, dtype=torch.float32, device=dev)
+    sel = torch.empty(nq, spec.top_k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+    osp = torch.empty_like(qs)
+    size_dt = "fp8" if dtype == "fp8" else torch.bfloat16
+    ws1 = torch.empty(hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k, size_dt),
+                      dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k, size_dt)),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        if dtype == "fp8":
+            hs2.full_attn_select_fp8kv(batch, q, k, v, spec.k_scale, spec.v_scale, spec.window, spec.top_k,
+                                       spec.scale, out=out, lse=lse, sel_idx=sel, sel_count=cnt, workspace=ws1)
+            hs2.sparse_attn_fp8kv(batch, qs, k, v, spec.k_scale, spec.v_scale, sel, spec.window, spec.top_k,
+                                  spec.scale, out=osp, workspace=ws2)
+        else:
+            hs2.full_attn_select(batch, q, k, v, spec.window, spec.top_k, spec.scale, out=out, lse=lse,
+                                 sel_idx=sel, sel_count=cnt, workspace=ws1)
+            hs2.sparse_attn(batch, qs, k, v, sel, spec.window, spec.top_k, spec.scale, out=osp, workspace=ws2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # eager reference (and warm-up) on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (out, lse, sel, cnt, osp)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    for _ in range(3):
+        for x in (out, osp):
+            x.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        sel.fill_(-7)
+        cnt.fill_(-7)
+        ws1.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (out, lse, sel, cnt, osp)):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
