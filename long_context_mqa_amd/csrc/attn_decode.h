@@ -44,8 +44,8 @@ struct AttnSmem {
   int32_t sel[kSelMax];
 };
 
-// Streams the tiles wave, wave + 4, ... of the workgroup's key range through the wave's
-// S = Kv::kStages LDS stages. DMA groups are issued in the order K0 V0 K1 V1 ..., then per
+// Streams the tiles ord.at(wave), ord.at(wave + kW), ... of the workgroup's key range
+// through the wave's S = Kv::kStages LDS stages. DMA groups are issued in the order K0 V0 K1 V1 ..., then per
 // tile K(it+S) right after the K operands of tile it are in registers and V(it+S) after
 // its PV step, so S tiles stream in while one is computed. Waits count the copies issued
 // later: constant in the steady state, and in the last S tiles a compile-time count per
@@ -55,7 +55,7 @@ struct AttnSmem {
 template <typename Kv, int kW, bool kMaxOnly, int kLater, bool kMore>
 __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& sm, const KeyList& kl, int k0, int k1,
                                    const void* __restrict__ kp, const void* __restrict__ vp, float c2, int wave,
-                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, int it) {
+                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, TileOrder ord, int it) {
   constexpr int S = stages_of<Kv, kW>(), D = Kv::kDma, T = Kv::kTileBytes;
   const int sidx = it % S;
   wait_vmcnt<D * (1 + 2 * kLater)>();  // K(it) has landed
@@ -63,9 +63,9 @@ __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& 
   bf16x8 kop[8];
   read_k_of<Kv>(kt, lane, kop);
   int rel;
-  const uint32_t vm = tile_rows(kl, k0 + (wave + it * kW) * kTile, k1, lane, rel);
+  const uint32_t vm = tile_rows(kl, k0 + ord.at(wave + it * kW) * kTile, k1, lane, rel);
   if (kMore) {
-    tile_rows(kl, k0 + (wave + (it + S) * kW) * kTile, k1, lane, rel);
+    tile_rows(kl, k0 + ord.at(wave + (it + S) * kW) * kTile, k1, lane, rel);
     issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * sidx) * T);
   }
   wait_vmcnt<D * (2 * kLater + (kMore ? 1 : 0))>();  // V(it) has landed
@@ -81,17 +81,17 @@ __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& 
 template <typename Kv, int kW, bool kMaxOnly, int kLater>
 __device__ inline void stream_tail(WaveState& st, float (&mx)[2], AttnSmem<kW>& sm, const KeyList& kl, int k0, int k1,
                                    const void* __restrict__ kp, const void* __restrict__ vp, float c2, int wave,
-                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, int ntw) {
+                                   int lane, const uint32_t (&vb)[4], uint32_t wbase, TileOrder ord, int ntw) {
   const int it = ntw - 1 - kLater;
-  if (it >= 0) stream_step<Kv, kW, kMaxOnly, kLater, false>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, it);
+  if (it >= 0) stream_step<Kv, kW, kMaxOnly, kLater, false>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, it);
   if constexpr (kLater > 0)
-    stream_tail<Kv, kW, kMaxOnly, kLater - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ntw);
+    stream_tail<Kv, kW, kMaxOnly, kLater - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, ntw);
 }
 
 template <typename Kv, int kW, bool kMaxOnly>
 __device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem<kW>& sm, const KeyList& kl, int k0, int k1,
                                     int ntiles, const void* __restrict__ kp, const void* __restrict__ vp,
-                                    float c2, int wave, int lane) {
+                                    float c2, int wave, int lane, TileOrder ord) {
   constexpr int S = stages_of<Kv, kW>(), T = Kv::kTileBytes;
   const int ntw = wave < ntiles ? (ntiles - wave + kW - 1) / kW : 0;
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
@@ -99,13 +99,13 @@ __device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem<kW>&
   vt_bases_of<Kv>(lane, vb);
   for (int it = 0; it < min(ntw, S); ++it) {
     int rel;
-    tile_rows(kl, k0 + (wave + it * kW) * kTile, k1, lane, rel);
+    tile_rows(kl, k0 + ord.at(wave + it * kW) * kTile, k1, lane, rel);
     issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * it) * T);
     issue_tile<Kv, false>(vp, kl.base, rel, lane, wbase + (2 * it + 1) * T);
   }
   for (int it = 0; it + S < ntw; ++it)
-    stream_step<Kv, kW, kMaxOnly, S - 1, true>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, it);
-  stream_tail<Kv, kW, kMaxOnly, S - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ntw);
+    stream_step<Kv, kW, kMaxOnly, S - 1, true>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, it);
+  stream_tail<Kv, kW, kMaxOnly, S - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, ntw);
 }
 
 template <typename Kv, bool kGather, int kW>
@@ -194,19 +194,21 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
 
   const void* kp = a.k;
   const void* vp = a.v;
+  // the gathered rows of a sparse split are few and random: no rotation there
+  const TileOrder ord = kGather ? TileOrder{0, ntiles} : TileOrder::rotated(i * a.n_split + split, ntiles);
   WaveState st;
   state_init(st);
   float mx[2] = {-INFINITY, -INFINITY};
-  stream_tiles<Kv, kW, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+  stream_tiles<Kv, kW, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane, ord);
   if (!state_finite(st)) {
     // rare: a logit far above the first tile's maximum overflowed the sums; recompute
     // with the exact maximum of this wave's keys as reference (every weight <= 1)
-    stream_tiles<Kv, kW, true>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+    stream_tiles<Kv, kW, true>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane, ord);
     state_init(st);
     st.m[0] = mx[0];
     st.m[1] = mx[1];
     st.have_ref = 1;
-    stream_tiles<Kv, kW, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane);
+    stream_tiles<Kv, kW, false>(st, mx, sm, kl, k0, k1, ntiles, kp, vp, a.c2, wave, lane, ord);
   }
 
 #pragma unroll

@@ -93,9 +93,13 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
 
   float* srow = a.scores + (size_t)i * a.score_stride;
   const int ntw = wave < ntiles ? (ntiles - wave + kSWaves - 1) / kSWaves : 0;
+  // Tiles in the reverse of the attention pass's rotated order (same rotation): the first
+  // tiles read here are the last that pass read, some still in the last-level cache.
+  const TileOrder ord = TileOrder::rotated(i * a.n_split + split, ntiles);
+  auto tile_of = [&](int x) { return ord.at(ntiles - 1 - x); };
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
   auto issue = [&](int it, int sidx) {
-    const int p = k0 + (wave + it * kSWaves) * kTile + (lane & 31);
+    const int p = k0 + tile_of(wave + it * kSWaves) * kTile + (lane & 31);
     const int rel = p < k1 ? p : 0;
     issue_tile<Kv, true>(a.k, base, rel, lane, wbase + sidx * Kv::kTileBytes);
   };
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
     // lane l and l^32 hold complementary heads of the same key; add in a fixed order
     const float other = __shfl_xor(sum, 32);
     const float total = (lane < 32) ? sum + other : other + sum;
-    const int p = k0 + (wave + it * kSWaves) * kTile + (lane & 31);
+    const int p = k0 + tile_of(wave + it * kSWaves) * kTile + (lane & 31);
     if (lane < 32 && p < k1) {
       sm.sbuf[wave][(it % kSFlush) * kTile + lane] = total;
       atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
       const int nt = it + 1 - first;
       for (int e = lane; e < nt * 8; e += 64) {
         const int tt = first + e / 8;
-        const int q0 = k0 + (wave + tt * kSWaves) * kTile + (e % 8) * 4;
+        const int q0 = k0 + tile_of(wave + tt * kSWaves) * kTile + (e % 8) * 4;
         const float4 v = *reinterpret_cast<const float4*>(&sm.sbuf[wave][(tt - first) * kTile + (e % 8) * 4]);
         if (q0 + 3 < k1) {
           *reinterpret_cast<float4*>(srow + q0) = v;
