@@ -12,9 +12,10 @@
 // weights are first transposed into the workspace (k contiguous), so that both MFMA
 // operands read 16 contiguous bytes per lane. Each workgroup computes a tile of 256 rows
 // x 384 columns (three output matrices; 256 when 2L is not a multiple of 3) of
-// C^T = W^T H^T with eight waves, two per SIMD, of 64 rows x 192 (128) columns. The
-// wider tile re-reads each H row 2L/3 times instead of L times and moves 17% fewer
-// operand bytes per MFMA; the tile's 192 accumulator registers per lane still allow two
+// C^T = W^T H^T with eight waves, two per SIMD, of 128 rows x 96 columns (64 x 128 for the
+// 256-column tile). The wider tile re-reads each H row 2L/3 times instead of L times; the
+// 128 x 96 wave tile reads 7 operand fragments from LDS per 12 MFMAs (8 for 64 x 192, which
+// measured 1.5-2% slower), and its 192 accumulator registers per lane still allow two
 // waves per SIMD. Operand tiles stream through two LDS stages 64 deep in the contraction
 // (80 KB each) by direct-to-LDS loads: one barrier per 64 of depth (half as many as with
 // 32-deep stages, which measured 15% slower on random data even with a third stage).
@@ -72,15 +73,14 @@ __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// kCols output columns per workgroup (256 or 384). Wave w: rows 64*(w%4) .. +63 of the
-// tile, columns (kCols/2)*(w/4) .. + kCols/2 - 1, as kXB x 2 blocks of 32 x 32.
+// kCols output columns per workgroup (256 or 384). Wave w: rows kWR*(w%kRW) .. of the
+// tile, columns kWC*(w/kRW) .., as kXB x kYB blocks of 32 x 32.
 template <int kCols>
 __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a) {
   constexpr int kTA = kCols * kKStep * 2;        // W^T tile bytes per stage
   constexpr int kTB = kBM * kKStep * 2;          // H tile bytes per stage
   constexpr int kCopA = kCols / kRowsPerCopy / kGWaves;  // 1 KB copies per wave per stage
   constexpr int kCopB = kBM / kRowsPerCopy / kGWaves;
-  constexpr int kXB = kCols / 64;                // 32-column blocks per wave
   static_assert(kCopA * kRowsPerCopy * kGWaves == kCols && kCopB * kRowsPerCopy * kGWaves == kBM,
                 "copies must split evenly");
   __shared__ __align__(16) uint8_t lds_a[kStagesG][kTA];
@@ -98,9 +98,12 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
   if (rt >= n_rt) return;
   const int64_t r0 = rt * kBM;
   const uint16_t* wt = a.wt + (size_t)nt * kCols * a.d_model;
-  const int wr = wave & 3;   // 64-row quarter
-  const int wc = wave >> 2;  // column half
-
+  // kCols == 384: 2 x 4 waves of 128 rows x 96 columns; kCols == 256: 4 x 2 of 64 x 128
+  constexpr int kRW = kCols == 384 ? 2 : 4;          // wave rows
+  constexpr int kWR = kBM / kRW;                     // rows per wave
+  constexpr int kWC = kCols / (kGWaves / kRW);       // columns per wave
+  const int wr = wave % kRW;
+  const int wc = wave / kRW;
   const uint32_t la0 = (uint32_t)(size_t)lds_a[0];
   const uint32_t lb0 = (uint32_t)(size_t)lds_b[0];
   // this wave's copies: A copies kCopA*wave + q, B copies kCopB*wave + q, kRowsPerCopy
@@ -128,11 +131,12 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
       dma16(gb[q] + kt * kKStep, lb0 + st * kTB + (kCopB * wave + q) * 1024);
   };
 
-  f32x16 acc[kXB][2];
+  constexpr int kXB = kWC / 32, kYB = kWR / 32;
+  f32x16 acc[kXB][kYB];
 #pragma unroll
   for (int x = 0; x < kXB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < kYB; ++y) acc[x][y] = f32x16{};
 
   const int KT = a.d_model / kKStep;  // >= 1 (d_model is a multiple of 64)
   static_assert(kStagesG == 2, "the loop below keeps one stage in flight");
@@ -146,29 +150,29 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
 #pragma unroll
     for (int ks = 0; ks < kKStep / 16; ++ks) {
       const int c = 2 * ks + (lane >> 5);
-      bf16x8 av[kXB], bv[2];
+      bf16x8 av[kXB], bv[kYB];
 #pragma unroll
       for (int x = 0; x < kXB; ++x)
-        av[x] = *reinterpret_cast<const bf16x8*>(lds_a[st] + op_off(wc * (kCols / 2) + 32 * x + (lane & 31), c));
+        av[x] = *reinterpret_cast<const bf16x8*>(lds_a[st] + op_off(wc * kWC + 32 * x + (lane & 31), c));
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-        bv[y] = *reinterpret_cast<const bf16x8*>(lds_b[st] + op_off(wr * 64 + 32 * y + (lane & 31), c));
+      for (int y = 0; y < kYB; ++y)
+        bv[y] = *reinterpret_cast<const bf16x8*>(lds_b[st] + op_off(wr * kWR + 32 * y + (lane & 31), c));
 #pragma unroll
       for (int x = 0; x < kXB; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < kYB; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
   }
 
   // C^T[n][row]: lane holds rows 32*y + l%32, columns 32*x + 8*(j/4) + 4*(l/32) + j%4
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int64_t grow = r0 + wr * 64 + 32 * y + (lane & 31);
+  for (int y = 0; y < kYB; ++y) {
+    const int64_t grow = r0 + wr * kWR + 32 * y + (lane & 31);
     if (grow >= a.n_rows) continue;
 #pragma unroll
     for (int x = 0; x < kXB; ++x) {
-      const int gc = nt * kCols + wc * (kCols / 2) + 32 * x;  // first output column of the block
+      const int gc = nt * kCols + wc * kWC + 32 * x;  // first output column of the block
       uint16_t* out = a.outs[gc / kDim];
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
