@@ -43,9 +43,10 @@
  *     returns a negative hs2_status, enqueues nothing and sets hs2_last_error().
  *     A failing launch returns HS2_ERR_HIP.
  *   - Device-side descriptor values are not read by the host. A query whose descriptor
- *     is inconsistent (q_pos outside [0, kv_len), rows outside [0, total_kv_rows))
- *     is not computed: its outputs are NaN and its sel_count is -1. No memory outside
- *     the given buffers is touched.
+ *     is inconsistent (q_pos outside [0, kv_len) or not below max_kv_len, rows outside
+ *     [0, total_kv_rows)) is not computed: its outputs are NaN and its sel_count is -1.
+ *     No memory outside the given buffers is touched. A kv_len_host value outside
+ *     [0, max_kv_len] returns HS2_ERR_INVALID_ARG.
  *   - Supported shapes: n_heads == 64, head_dim == 128 (the MQA layout of the pages,
  *     [arex] "Numbers computed on three 80B-A3B models"); anything else returns
  *     HS2_ERR_UNSUPPORTED. 1 <= window <= 1<<18, 0 <= top_k <= HS2_MAX_TOP_K.

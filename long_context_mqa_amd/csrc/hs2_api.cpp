@@ -218,6 +218,12 @@ hs2_status check_batch(const hs2_seqs* b) {
   if (!aligned(b->kv_start, 8) || !aligned(b->kv_len, 4) || !aligned(b->q_start, 4) ||
       (b->q_pos && !aligned(b->q_pos, 4)))
     return fail(HS2_ERR_INVALID_ARG, "batch descriptor arrays are misaligned");
+  if (b->kv_len_host) {  // the split planner sizes work items from these
+    for (int s = 0; s < b->num_seqs; ++s)
+      if (b->kv_len_host[s] < 0 || b->kv_len_host[s] > b->max_kv_len)
+        return fail(HS2_ERR_INVALID_ARG, "kv_len_host[%d] = %d is outside [0, max_kv_len = %d]", s,
+                    b->kv_len_host[s], b->max_kv_len);
+  }
   return HS2_OK;
 }
 
@@ -253,6 +259,7 @@ SeqsDev to_dev(const hs2_seqs* b) {
   d.num_seqs = b->num_seqs;
   d.total_q = b->total_q;
   d.total_rows = b->total_kv_rows;
+  d.max_kv_len = b->max_kv_len;
   return d;
 }
 

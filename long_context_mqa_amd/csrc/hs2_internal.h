@@ -32,6 +32,7 @@ struct SeqsDev {
   int32_t num_seqs;
   int32_t total_q;
   int64_t total_rows;
+  int32_t max_kv_len;  // the host's bound of every kv_len, which sizes splits and score rows
 };
 
 // Partial result of one workgroup's key range for one query: running max m (log2
@@ -158,7 +159,8 @@ struct AppendArgs {
 };
 
 // Resolves query i: sequence row base and position t. Returns false when the
-// descriptor is inconsistent (the query is then not computed). The sequence is first
+// descriptor is inconsistent (the query is then not computed), which includes a position
+// at or beyond max_kv_len: the key splits and score rows are sized from that bound. The sequence is first
 // guessed proportionally (exact for batches with equal query counts per sequence), and
 // found by binary search over q_start otherwise.
 __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t) {
@@ -175,8 +177,8 @@ __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t
   base = b.kv_start[lo];
   const int n = b.kv_len[lo];
   t = b.q_pos[i];
-  const bool ok = b.q_start[lo] <= i && i < b.q_start[lo + 1] && t >= 0 && t < n && base >= 0 &&
-                  base + (int64_t)n <= b.total_rows;
+  const bool ok = b.q_start[lo] <= i && i < b.q_start[lo + 1] && t >= 0 && t < n && t < b.max_kv_len &&
+                  base >= 0 && base + (int64_t)n <= b.total_rows;
   if (!ok) { base = 0; t = 0; }
   return ok;
 }

@@ -79,6 +79,23 @@ def test_select_rejects_bad_arguments(lib):
     assert _select(lib, bad) == hs2.HS2_ERR_INVALID_ARG
 
 
+def test_host_lengths_beyond_max_kv_len_are_rejected(lib):
+    """The split planner sizes its work items from kv_len_host; a value above the
+    max_kv_len bound (or negative) is an invalid argument, for selection and sparse calls."""
+    import numpy as np
+    for lens in ([4096, 4097], [-1, 100]):
+        kh = np.asarray(lens, dtype=np.int32)
+        b = hs2.hs2_seqs(2, FAKE, FAKE, FAKE, FAKE, 2, 4096, 8193, 1, kh.ctypes.data)
+        assert _select(lib, b, ws_bytes=1 << 40) == hs2.HS2_ERR_INVALID_ARG
+        assert b"kv_len_host" in lib.hs2_last_error()
+        assert lib.hs2_sparse_attn(ctypes.byref(b), FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 128, 128, 1024, 0.088,
+                                   FAKE * 5, None, FAKE * 6, 1 << 40, hs2.HS2_BF16, None) == hs2.HS2_ERR_INVALID_ARG
+        assert b"kv_len_host" in lib.hs2_last_error()
+    kh = np.asarray([4096, 17], dtype=np.int32)  # within the bound: accepted by the host checks
+    b = hs2.hs2_seqs(2, FAKE, FAKE, FAKE, FAKE, 2, 4096, 8193, 1, kh.ctypes.data)
+    assert _select(lib, b, ws_bytes=16) == hs2.HS2_ERR_WORKSPACE  # fails later, at the workspace size
+
+
 def test_sparse_rejects_bad_arguments(lib):
     b = _batch()
     ws = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, 128, 1024, 0)

@@ -248,6 +248,38 @@ def test_invalid_descriptor_is_not_computed():
     check_selection(g["sel"][0], int(g["count"][0]), r, spec.top_k, 3000 - 127, "valid neighbour")
 
 
+def test_position_beyond_max_kv_len_is_not_computed():
+    """max_kv_len sizes the key splits and the score rows: a query at or beyond it (its
+    sequence longer than the bound) is skipped like any inconsistent descriptor, nothing
+    is written outside the workspace, and the other query is unaffected."""
+    spec = BlockSpec("beyond", [3000, 5000], [[2999], [4999]], dtype="bf16", n_sparse=1, needles_per_query=0,
+                     seed=19)
+    inp = make_block_inputs(spec)
+    dev = "cuda"
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, dev)
+    batch.max_kv_len = 4000   # below sequence 1's length; its query sits at 4999
+    batch.kv_len_host = None  # (a host copy above the bound is rejected on the host)
+    k, v, q, qs = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel), to_dev(inp.q_sp[0])
+    guard = 1 << 16
+    n1 = hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k)
+    n2 = max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k))
+    ws1 = torch.full((n1 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    ws2 = torch.full((n2 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    out, lse, sel, cnt = hs2.full_attn_select(batch, q, k, v, spec.window, spec.top_k, spec.scale,
+                                              workspace=ws1[:n1])
+    o, _ = hs2.sparse_attn(batch, qs, k, v, sel, spec.window, spec.top_k, spec.scale, workspace=ws2[:n2])
+    torch.cuda.synchronize()
+    assert bool((ws1[n1:] == 0x5A).all()) and bool((ws2[n2:] == 0x5A).all())
+    g_out, g_sel, g_cnt, g_sp = from_dev(out), sel.cpu().numpy(), cnt.cpu().numpy(), from_dev(o)
+    assert int(g_cnt[1]) == -1 and np.all(g_sel[1] == -1)
+    assert np.isnan(g_out[1]).all() and np.isnan(g_sp[1]).all()
+    r = oracle_query(inp, 0)
+    check_attn(g_out[0], r["out"], "query below the bound")
+    check_selection(g_sel[0], int(g_cnt[0]), r, spec.top_k, 3000 - 127, "query below the bound")
+    ref, _ = oracle_sparse(inp, 0, 0, g_sel[0], r["K"], r["V"])
+    check_attn(g_sp[0], ref, "query below the bound, sparse layer")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_repeat_runs_are_bitwise_identical(dtype):
     inp = make_block_inputs(BlockSpec("det", [20000, 7000], [[19999], [6999, 3000]], dtype=dtype, n_sparse=1,
