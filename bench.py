@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8, 9])
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-1m", action="store_true", help="workload 2 only: skip the 1M-context sub-record")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy 3 times (counter calibration) and exit")
     return p.parse_args()
@@ -62,7 +63,7 @@ def parse():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("attn_decode.h", "attn_common.h", "hs2_internal.h"):
+    for f in ("attn_decode.h", "attn_common.h", "kernel_common.h", "hs2_internal.h"):
         with open(os.path.join(ROOT, "long_context_mqa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -84,7 +85,6 @@ def counter_traffic(per_launch_keys: int):
 def cpu_baseline(inp, budget_s: float):
     """The fp64 oracle, unchanged, on a bounded sample of the same workload's queries."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import oracle
     from workloads.gen import stored_to_f64
@@ -110,10 +110,30 @@ def cpu_baseline(inp, budget_s: float):
         done += 1
         if spent >= budget_s:
             break
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / spent, "unit": "tokens/s", **host_cores(), "kind": "oracle",
             "sample": f"{done} of {sp.total_q} queries of {sp.name} (selector + {sp.n_sparse} sparse layers "
                       f"each, fp64, {spent:.1f} s)"}
+
+
+def host_cores() -> dict:
+    """Threads the oracle ran on (numpy's BLAS pool: the matrix products are its only
+    multi-threaded steps), the host's logical CPUs and the CPU model name."""
+    from threadpoolctl import threadpool_info
+
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    model = ""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        model = next((l.split(":", 1)[1].strip() for l in out.splitlines() if l.startswith("Model name")), "")
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cores": int(min(threads, affinity)), "host_cpus": os.cpu_count(), "cpus_in_affinity": affinity,
+            "cpu_model": model}
 
 
 def to_dev(a, device="cuda"):
@@ -154,8 +174,28 @@ def main() -> int:
         return run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs)
     if args.workload == 9:
         return run_v1(args, hs2)
-    append = args.workload == 8
-    spec = block_config(2 if append else args.workload)
+    res = run_decode(args, hs2, args.workload, args.steps, args.warmup, args.cpu_seconds)
+    if args.workload == 2 and not args.no_1m:
+        # the same step at 1M context (8 sequences x 1,048,576 tokens): a sub-record, not the value
+        log("1M context: decode-8x1M-bf16")
+        r = run_decode(args, hs2, 3, max(5, min(args.steps, 20)), min(args.warmup, 3), min(args.cpu_seconds, 12.0))
+        res["decode_1m"] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "roofline", "block",
+                                             "kernels_ms", "sparse_layer", "cpu_baseline")}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_decode(args, hs2, workload: int, steps: int, warmup: int, cpu_seconds: float) -> dict:
+    """Decode-shaped and chunked workloads: a step is the selector plus every sparse
+    layer (workload 5: after the KV Bridging of 1,048,576 hidden states; workload 8: after
+    the decode-time bridging of the batch's new tokens). Returns the JSON record."""
+    import numpy as np
+    import torch
+
+    from workloads.configs import block_config, make_bridge_inputs, make_block_inputs
+
+    append = workload == 8
+    spec = block_config(2 if append else workload)
     log(f"generating {spec.name}")
     inp = make_block_inputs(spec)
     dev = torch.device("cuda:0")
@@ -193,7 +233,7 @@ def main() -> int:
                             workspace=ws_sp)
     outs = [torch.empty_like(q_sel) for _ in range(spec.n_sparse)]
     bridge = None
-    if args.workload == 5:
+    if workload == 5:
         log("generating bridging inputs (1,048,576 x 2048)")
         bi = make_bridge_inputs(1048576, n_layers=3, seed=5)
         bridge = {"h": to_dev(bi.h), "wk": [to_dev(w) for w in bi.w_k], "wv": [to_dev(w) for w in bi.w_v]}
@@ -201,6 +241,17 @@ def main() -> int:
         bridge["vo"] = [torch.empty(1048576, 128, dtype=torch.bfloat16, device=dev) for _ in range(3)]
         bridge["ws"] = torch.empty(hs2.bridge_kv_workspace_size(2048, 3), dtype=torch.uint8, device=dev)
         del bi
+        # the decode runs on the bridged caches: sequence s takes bridged layer-0 rows
+        # (o_s + j) mod 1,048,576 (o_s = the rows of the sequences before it), copied once,
+        # untimed, into its packed rows; the planted needle rows are written on top
+        hs2.bridge_kv(bridge["h"], bridge["wk"], bridge["wv"], bridge["ko"], bridge["vo"], workspace=bridge["ws"])
+        src = torch.from_numpy(np.arange(spec.total_rows, dtype=np.int64) % 1048576).to(dev)
+        k.copy_(bridge["ko"][0].index_select(0, src))
+        v.copy_(bridge["vo"][0].index_select(0, src))
+        nrow = torch.from_numpy(np.asarray([int(inp.kv_start[si]) + p for (si, _, _, p) in inp.needles],
+                                           dtype=np.int64)).to(dev)
+        k.index_copy_(0, nrow, to_dev(inp.k[nrow.cpu().numpy()]))
+        del src, nrow
     if append:
         # decode-time bridging: the 64 new tokens' hidden states into the current-token
         # rows of 3 layers' caches (layer 0's are the block's K and V)
@@ -247,8 +298,8 @@ def main() -> int:
             sparse_call(l)
         hs2.set_kernel_events(None)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -256,7 +307,7 @@ def main() -> int:
     # (selector pass 1; the bridging GEMM when bridging is part of the step): a pair of
     # events around every kernel would lengthen the step by ~10%.
     roof_events = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         n_ev = 4 if bridge is not None else 2
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         for e in evs:
@@ -278,13 +329,13 @@ def main() -> int:
         for l in range(spec.n_sparse):
             sparse_call(l)
 
-    log(f"timing {args.steps} steps")
+    log(f"timing {steps} steps")
     t0 = time.perf_counter()
-    for s_ in range(args.steps):
+    for s_ in range(steps):
         timed_step(roof_events[s_])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_step = elapsed / args.steps * 1e3
+    ms_step = elapsed / steps * 1e3
     if bridge is not None:
         roof_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in roof_events]))
     else:
@@ -292,7 +343,7 @@ def main() -> int:
 
     # Per-kernel breakdown: an instrumented pass after the timed steps (events around
     # every kernel), not part of the timed figure.
-    n_prof = min(args.steps, 10)
+    n_prof = min(steps, 10)
     ev = [(new_events(5), [new_events(2) for _ in range(spec.n_sparse)], new_events(2) if bridge else None,
            new_events(1) if append else None)
           for _ in range(n_prof)]
@@ -318,26 +369,71 @@ def main() -> int:
         kern["bridge_gemm"] = mean_ms(br, 1)
     if append:
         kern["bridge_append"] = mean_ms([e[3] for e in ev], 0)
-    sparse_layer_ms = (kern.get("sparse_attn") or 0.0) + (kern.get("sparse_combine") or 0.0)
 
     # algorithmic work
     keys = int(sum(int(t) + 1 for t in inp.q_pos))
     cands = int(sum(max(0, int(t) - spec.window + 1) for t in inp.q_pos))
     attended = int(sum(min(int(t) + 1, spec.window + spec.top_k) for t in inp.q_pos))
-    sel_bytes = keys * kv_row_bytes if nq == spec.total_q and all(len(p) == 1 for p in spec.q_positions) \
-        else spec.total_rows * kv_row_bytes
-    sparse_bytes = spec.n_sparse * (attended * kv_row_bytes + nq * QO_BYTES)
+    decode = all(len(p) == 1 for p in spec.q_positions)
+    sel_bytes = keys * kv_row_bytes if decode else spec.total_rows * kv_row_bytes
+    layer_bytes = attended * kv_row_bytes + nq * QO_BYTES      # one sparse layer: gathered K+V rows, Q and O
+    sparse_bytes = spec.n_sparse * layer_bytes
     step_bytes = sel_bytes + sparse_bytes
     flops_attn = keys * QK_PV_FLOPS + spec.n_sparse * attended * QK_PV_FLOPS
     flops_score = cands * SCORE_FLOPS
-    decode = all(len(p) == 1 for p in spec.q_positions)
+
+    # Sparse layer, warm and cold: a whole hs2_sparse_attn call (attention + split combine)
+    # between two events, with no event between its kernels. Warm: right after another
+    # sparse layer of the same step, whose gathered rows are then in the 256 MB
+    # last-level cache (MALL) and the L2s. Cold: after a 512 MiB read-modify-write, which
+    # evicts them both. The attention kernel alone, cold, comes from a second set of calls
+    # with the library's events around each kernel.
+    sparse_rec = None
+    if spec.n_sparse:
+        flush = torch.zeros(128 << 20, dtype=torch.int32, device=dev)   # 512 MiB
+        reps = 10
+        pairs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        kev = [new_events(2) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for r_ in range(reps):
+            e = pairs[r_]
+            flush.add_(1)
+            e[0].record()
+            sparse_call(0)
+            e[1].record()
+            e[2].record()
+            sparse_call(1 % spec.n_sparse)
+            e[3].record()
+        for r_ in range(reps):
+            flush.add_(1)
+            attach(kev[r_])
+            sparse_call(0)
+            hs2.set_kernel_events(None)
+        torch.cuda.synchronize()
+        del flush
+        cold_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in pairs]))
+        warm_us = float(np.median([e[2].elapsed_time(e[3]) * 1e3 for e in pairs]))
+        cold_att = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in kev]))
+        sparse_rec = {"alg_bytes": layer_bytes, "bound": "hbm", "peak_gbps": HBM_PEAK_GBPS,
+                      "warm_us": warm_us, "warm_gbps": layer_bytes / (warm_us * 1e-6) / 1e9,
+                      "warm_frac": layer_bytes / (warm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                      "cold_us": cold_us, "cold_gbps": layer_bytes / (cold_us * 1e-6) / 1e9,
+                      "cold_frac": layer_bytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                      "cold_attn_kernel_us": cold_att,
+                      "warm_kernels_us": {"attn": (kern.get("sparse_attn") or 0.0) * 1e3,
+                                          "combine": (kern.get("sparse_combine") or 0.0) * 1e3},
+                      "method": "median of 10 calls, each between two events (attention + split combine); cold "
+                                "after a 512 MiB read-modify-write that evicts the L2s and the 256 MB MALL, warm "
+                                "right after another sparse layer on the same rows; warm_kernels_us from the "
+                                "per-kernel events of the instrumented steps"}
+
     res = {
         "metric": METRIC,
-        "value": nq / (elapsed / args.steps),
+        "value": nq / (elapsed / steps),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -350,8 +446,10 @@ def main() -> int:
                    "top_k": spec.top_k, "q_heads": 64, "kv_heads": 1, "head_dim": 128,
                    "parallelism": "single GPU"},
     }
-    if args.workload == 5:
+    if workload == 5:
         res["config"]["bridging"] = {"rows": 1048576, "d_model": 2048, "layers": 3}
+        res["data"] = ("synthetic: seeded N(0,1) hidden states and Q (bf16), weights N(0, 0.02^2); the decode "
+                       "runs on the bridged layer-0 K/V with planted needle keys")
     if append:
         res["config"]["workload"] = "decode-64x128k-bf16+bridging-append"
         res["config"]["bridging_append"] = {"new_tokens": nq, "d_model": 2048, "layers": 3,
@@ -371,7 +469,7 @@ def main() -> int:
         res["roofline"] = {"kernel": "attn_pass1 (selector exact attention, K+V once)", "bound": "hbm",
                            "achieved": a_bytes / (roof_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                            "unit": "GB/s", "frac": a_bytes / (roof_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                           "traffic": counter_traffic(keys) if args.workload == 2 else None,
+                           "traffic": counter_traffic(keys) if workload == 2 else None,
                            "alg_bytes_per_launch": a_bytes, "avg_launch_ms": roof_ms}
     else:
         f = keys * QK_PV_FLOPS
@@ -388,8 +486,7 @@ def main() -> int:
     }
     res["kernels_ms"] = kern
     res["kernels_ms_source"] = f"HIP events around every kernel over {n_prof} steps after the timed ones"
-    res["sparse_layer_gbps_alg"] = (attended * kv_row_bytes + nq * QO_BYTES) / (
-        sparse_layer_ms * 1e-3) / 1e9 if spec.n_sparse else None
+    res["sparse_layer"] = sparse_rec
     if bridge is not None:
         bf = 2 * 1048576 * 2048 * 256 * 3
         res["bridging"] = {"ms": kern["bridge_gemm"], "tflops": bf / (kern["bridge_gemm"] * 1e-3) / 1e12,
@@ -397,9 +494,8 @@ def main() -> int:
     res["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu baseline)")
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
-    return 0
+        res["cpu_baseline"] = cpu_baseline(inp, cpu_seconds)
+    return res
 
 
 def run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs) -> int:
@@ -415,6 +511,10 @@ def run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs) 
     dev = torch.device("cuda:0")
     batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, n, dev)
     k, v, q = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel)
+    # what the oracle's timing needs: the caches and the query rows of an even grid of positions
+    grid = np.linspace(0, n - 1, 4096).astype(np.int64)
+    np.random.default_rng(0).shuffle(grid)
+    cpu_in = (inp.k, inp.v, grid, inp.q_sel[grid].copy())
     del inp
     out = torch.empty_like(q)
     lse = torch.empty(n, 64, dtype=torch.float32, device=dev)
@@ -485,14 +585,47 @@ def run_prefill(args, hs2, block_config, make_block_inputs, make_bridge_inputs) 
                      "frac_mfma": f_br / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample (cpu baseline)")
+        res["cpu_baseline"] = cpu_baseline_prefill(spec, *cpu_in, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def cpu_baseline_prefill(spec, k_stored, v_stored, grid, q_rows, budget_s: float):
+    """The fp64 oracle, unchanged, on evenly spaced positions of the prefill: the bridging
+    of the position's hidden state into 3 layers' K/V, then its exact causal attention.
+    Positions are visited in a shuffled order of an even grid over [0, n) (`grid`, with
+    their query rows `q_rows`), so the mean cost of the visited ones is that of the whole
+    prefill."""
+    import oracle
+    from workloads.configs import make_bridge_inputs
+    from workloads.gen import stored_to_f64
+
+    n = spec.total_rows
+    K, V = stored_to_f64(k_stored), stored_to_f64(v_stored)
+    bi = make_bridge_inputs(64, n_layers=3, seed=7)
+    wk = [stored_to_f64(w) for w in bi.w_k]
+    wv = [stored_to_f64(w) for w in bi.w_v]
+    h = stored_to_f64(bi.h)
+    done, spent = 0, 0.0
+    for t, qrow in zip(grid, q_rows):
+        q = stored_to_f64(qrow)
+        t0 = time.perf_counter()
+        oracle.bridge_kv(h[done % 64:done % 64 + 1], wk, wv)
+        oracle.full_attention(q, K, V, int(t), spec.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tokens/s", **host_cores(), "kind": "oracle",
+            "sample": f"{done} of {n} positions of {spec.name}, evenly spaced (bridging of one hidden state into "
+                      f"3 layers' K/V + exact causal attention of the position, fp64, {spent:.1f} s)"}
 
 
 def cpu_baseline_v1(inp, budget_s: float):
     """The fp64 first-generation oracle, unchanged, on a bounded sample of the queries."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import hysparse_v1 as ov1
     from workloads.gen import stored_to_f64
@@ -527,8 +660,7 @@ def cpu_baseline_v1(inp, budget_s: float):
         done += 1
         if spent >= budget_s:
             break
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / spent, "unit": "tokens/s", **host_cores(), "kind": "oracle",
             "sample": f"{done} of {sp.total_q} queries of {sp.name} (selector + {sp.n_sparse} sparse layers "
                       f"each, fp64, {spent:.1f} s)"}
 

@@ -35,7 +35,8 @@
  *   - Selected indices are sequence-local candidate positions, ascending, padded with -1.
  *   - LSE outputs are natural-log log-sum-exp of the scaled logits, fp32.
  *   - The caller owns every buffer and the stream. The library allocates nothing, keeps
- *     no state between calls and never synchronises the stream. Inputs are read-only;
+ *     no state between calls (apart from the per-thread attachment of the measurement
+ *     hook hs2_set_kernel_events) and never synchronises the stream. Inputs are read-only;
  *     outputs and the workspace must not alias any input or each other.
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and the call
  *     returns; device faults surface at the caller's next synchronisation.
@@ -87,7 +88,11 @@ typedef struct hs2_seqs {
   const int64_t* kv_start; /* device [num_seqs]: first row of sequence s in K and V         */
   const int32_t* kv_len;   /* device [num_seqs]: n_s, cached rows of s (current token incl.)*/
   const int32_t* q_start;  /* device [num_seqs+1]: queries of s are rows q_start[s] ..
-                              q_start[s+1]-1 of Q; q_start[0] == 0, non-decreasing          */
+                              q_start[s+1]-1 of Q; q_start[0] == 0, non-decreasing,
+                              q_start[num_seqs] == total_q (otherwise every query is
+                              inconsistent; a q_start that decreases somewhere leaves the
+                              results of the queries it covers undefined, never touching
+                              memory outside the given buffers)                          */
   const int32_t* q_pos;    /* device [total_q]: position t of each query, 0 <= t < n_s      */
   int32_t total_q;         /* host: q_start[num_seqs]                                      */
   int32_t max_kv_len;      /* host: an upper bound of every kv_len                         */
@@ -97,7 +102,10 @@ typedef struct hs2_seqs {
                               split of each query's keys over workgroups when every
                               sequence has at most one query (ragged decode); without it
                               the split assumes equal lengths, which may leave a second,
-                              mostly idle round of workgroups                            */
+                              mostly idle round of workgroups. It must not be below the
+                              device kv_len (also for every replay of a captured call):
+                              a query whose keys run past the workgroups planned from it
+                              is reported as inconsistent (NaN outputs, sel_count -1) */
 } hs2_seqs;
 
 /* Library version: HS2_VERSION of the built library. */
@@ -343,7 +351,9 @@ hs2_status hs2_v1_sparse_attn(const hs2_seqs* batch, const void* q, const void* 
 
 /* ------------------------------------------------------------------------------------
  * Kernel timing hook, for benchmarks and profilers that need per-kernel durations on the
- * library's own stream (not an operation of the method). While attached, every hs2_*
+ * library's own stream (not an operation of the method, and the one exception to "no
+ * state between calls": an attachment lasts until it is detached, on the thread that
+ * made it, and changes no result). While attached, every hs2_*
  * compute call records events[2*j] right before and events[2*j+1] right after its
  * kernel of pipeline slot j (j < n_pairs), on that call's stream. Slots:
  *   hs2_full_attn_select: 0 attention, 1 split combine, 2 score pass, 3 top-k filter,
@@ -355,8 +365,8 @@ hs2_status hs2_v1_sparse_attn(const hs2_seqs* batch, const void* q, const void* 
  * A slot whose kernel a call does not need (e.g. no split combine when one workgroup
  * covers a query) is not recorded. The events are hipEvent_t handles created and owned
  * by the caller and must stay valid while attached. events == NULL or n_pairs == 0
- * detaches. Process-wide and not synchronised: attach and detach only while no other
- * thread calls the library. 0 <= n_pairs <= 16.
+ * detaches. The attachment is per calling thread: calls made on other threads record
+ * nothing. 0 <= n_pairs <= 16.
  * ------------------------------------------------------------------------------------ */
 hs2_status hs2_set_kernel_events(void* const* events, int32_t n_pairs);
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   int64_t base;
   int t;
-  const bool valid = query_desc(a.b, i, base, t);
+  const bool valid = query_desc(a.b, i, base, t) && !(a.plan_miss != nullptr && a.plan_miss[i] != 0);
   OutT* out = static_cast<OutT*>(a.out) + (size_t)i * kHeads * kDim;
   const int d0 = slab * 16 + grp * 4;
   if (!valid) {

@@ -72,9 +72,9 @@ __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles,
   for (int s0 = 0; s0 < b.num_seqs; s0 += 256) {
     const int s = s0 + threadIdx.x;
     int q0 = 0, nq = 0;
-    if (s < b.num_seqs) {
-      q0 = b.q_start[s];
-      nq = max(0, b.q_start[s + 1] - q0);
+    if (s < b.num_seqs) {  // the tiles stay within the rows of Q: [0, total_q)
+      q0 = min(max(b.q_start[s], 0), b.total_q);
+      nq = max(0, min(b.q_start[s + 1], b.total_q) - q0);
     }
     const uint32_t cnt = (uint32_t)((nq + kQT - 1) / kQT);
     uint32_t total;

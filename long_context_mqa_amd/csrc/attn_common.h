@@ -3,7 +3,7 @@
 // step on the matrix cores. See attn_bf16.hip for the layout of the MFMA operands.
 #pragma once
 
-#include "hs2_internal.h"
+#include "kernel_common.h"
 
 namespace hs2 {
 namespace attn {

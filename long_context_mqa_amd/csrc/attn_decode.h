@@ -156,6 +156,8 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
     for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) hist[(size_t)i * kHistBins + e] = 0u;
     if (threadIdx.x < 4) counters[(size_t)i * 4 + threadIdx.x] = 0u;
   }
+  if (!kGather && wl.n > 0 && a.plan_miss != nullptr && threadIdx.x == 0 && last_planned(wl, i))
+    a.plan_miss[i] = (valid && k0 + a.split_keys < t + 1) ? 1 : 0;
   if (!valid) {
     if (a.n_split == 1) {
       __bf16* out = static_cast<__bf16*>(a.out) + (size_t)i * kHeads * kDim;

@@ -10,7 +10,7 @@
 //
 // Thread layout: 256 threads = 64 heads x 4 slices of 32 dims. A logit is the sum of the
 // four slice dot products (two xor-shuffles within the four lanes of a head).
-#include "hs2_internal.h"
+#include "kernel_common.h"
 
 namespace hs2 {
 namespace {

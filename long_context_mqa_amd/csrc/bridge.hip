@@ -21,7 +21,7 @@
 // 32-deep stages, which measured 15% slower on random data even with a third stage).
 // Tiles of the same rows run back to back on one XCD, so H is read from HBM once and
 // re-served from that XCD's L2 for the other column tiles.
-#include "hs2_internal.h"
+#include "kernel_common.h"
 
 namespace hs2 {
 namespace {

@@ -71,12 +71,14 @@ Split plan_split(int64_t work, int64_t max_keys) {
 // keys_s = n_s - sub (clamped at 0).
 bool plan_split_lengths(const hs2_seqs* b, int64_t sub, int64_t max_keys, Split& out, WorkList* wl) {
   if (!b->kv_len_host || b->max_q_per_seq > 1 || max_keys <= 0) return false;
+  // every query gets at least one workgroup: the one that reports a length beyond the plan
+  auto splits_of = [&](int s, int64_t sk) {
+    const int64_t k = std::max<int64_t>(0, (int64_t)b->kv_len_host[s] - sub);
+    return std::max<int64_t>(1, ceil_div(k, sk));
+  };
   auto active = [&](int64_t sk) {
     int64_t n = 0;
-    for (int s = 0; s < b->num_seqs; ++s) {
-      const int64_t k = std::max<int64_t>(0, (int64_t)b->kv_len_host[s] - sub);
-      n += ceil_div(k, sk);
-    }
+    for (int s = 0; s < b->num_seqs; ++s) n += splits_of(s, sk);
     return n;
   };
   const int64_t hi_tiles = ceil_div(max_keys, kTile);
@@ -101,8 +103,7 @@ bool plan_split_lengths(const hs2_seqs* b, int64_t sub, int64_t max_keys, Split&
     wl->n = 0;
     if (b->total_q == b->num_seqs && active(out.split_keys) <= kMaxWorkItems && out.n_split <= 512) {
       for (int q = 0; q < b->num_seqs; ++q) {
-        const int64_t k = std::max<int64_t>(0, (int64_t)b->kv_len_host[q] - sub);
-        const int64_t ns = ceil_div(k, out.split_keys);
+        const int64_t ns = splits_of(q, out.split_keys);
         for (int64_t sp = 0; sp < ns; ++sp) wl->item[wl->n++] = ((uint32_t)q << 9) | (uint32_t)sp;
       }
     }
@@ -127,7 +128,8 @@ struct SelectPlan {
   int f_split = 1, f_len = kFilterLen;
   int64_t score_stride = 0;
   size_t off_part = 0, off_lse2 = 0, off_scores = 0, off_hist = 0, off_counters = 0,
-         off_above = 0, off_cand = 0, total = 0;
+         off_above = 0, off_cand = 0, off_miss = 0, total = 0;
+  bool lists() const { return attn_wl.n > 0 || score_wl.n > 0; }
 };
 
 // selection == false: exact causal attention only (hs2_causal_attn): no LSE copy, score
@@ -175,6 +177,10 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt, b
   if (p.chunk) {
     p.off_tiles = off;
     off += align_up((size_t)p.max_tiles * sizeof(int2));
+  }
+  if (p.lists()) {  // plan-miss flags of the work-list launches: attention, then score pass
+    p.off_miss = off;
+    off += align_up((size_t)2 * tq * sizeof(int32_t));
   }
   if (top_k > 0) {
     p.off_scores = off;
@@ -263,10 +269,10 @@ SeqsDev to_dev(const hs2_seqs* b) {
   return d;
 }
 
-// Kernel timing hook state (see hs2_set_kernel_events).
+// Kernel timing hook state (see hs2_set_kernel_events): per calling thread.
 constexpr int kMaxEventPairs = 16;
-hipEvent_t g_events[2 * kMaxEventPairs];
-int g_event_pairs = 0;
+thread_local hipEvent_t g_events[2 * kMaxEventPairs];
+thread_local int g_event_pairs = 0;
 
 // Brackets the kernel of pipeline slot j of one entry-point call with the attached events.
 struct LaunchMarks {
@@ -378,6 +384,8 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   a.lse = lse;
   a.lse2 = lse2;
   a.v_scale = fp8 ? v_scale : 1.0f;
+  int32_t* miss = p.lists() ? at<int32_t>(workspace, p.off_miss) : nullptr;
+  a.plan_miss = p.attn_wl.n > 0 ? miss : nullptr;
   const int grid = tq * p.attn.n_split;
   int2* tiles = p.chunk ? at<int2>(workspace, p.off_tiles) : nullptr;
   LaunchMarks mk(s);
@@ -415,6 +423,7 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     c.hist = hist;
     c.counters = counters;
     c.v_scale = a.v_scale;
+    c.plan_miss = a.plan_miss;
     e = mk.before(1);
     if (e == hipSuccess) e = launch_combine(c, f32, s);
     if (e == hipSuccess) e = mk.after(1);
@@ -434,6 +443,11 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   tk.cand = top_k > 0 ? at<uint2>(workspace, p.off_cand) : nullptr;
   tk.sel_idx = sel_idx;
   tk.sel_count = sel_count;
+  tk.miss_attn = a.plan_miss;
+  tk.miss_score = top_k > 0 && p.score_wl.n > 0 ? miss + tq : nullptr;
+  tk.out = out;
+  tk.lse = lse;
+  tk.out_f32 = f32 ? 1 : 0;
   if (top_k > 0) {
     ScoreArgs sc{};
     sc.b = a.b;
@@ -448,6 +462,7 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     sc.score_stride = p.score_stride;
     sc.scores = at<float>(workspace, p.off_scores);
     sc.hist = hist;
+    sc.plan_miss = tk.miss_score ? miss + tq : nullptr;
     e = mk.before(2);
     if (e == hipSuccess) {
       if (p.chunk)
@@ -574,6 +589,7 @@ hs2_status causal_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   a.lse2 = nullptr;
   a.v_scale = 1.0f;
   a.direct = p.chunk && p.attn.n_split == 1;
+  a.plan_miss = p.attn_wl.n > 0 ? at<int32_t>(workspace, p.off_miss) : nullptr;
   const int grid = batch->total_q * p.attn.n_split;
   LaunchMarks mk(s);
   hipError_t e = hipSuccess;
@@ -608,6 +624,7 @@ hs2_status causal_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     c.hist = nullptr;
     c.counters = nullptr;
     c.v_scale = 1.0f;
+    c.plan_miss = a.plan_miss;
     e = mk.before(1);
     if (e == hipSuccess) e = launch_combine(c, f32, s);
     if (e == hipSuccess) e = mk.after(1);

@@ -1,4 +1,6 @@
-// Internal declarations shared by the HIP kernels and the host entry points of libhs2.
+// Internal declarations shared by the HIP kernels and the host entry points of libhs2:
+// constants, kernel argument structs and the launchers. Host-only code (the entry points
+// in hs2_api.cpp) includes just this file; the device helpers are in kernel_common.h.
 // Target: gfx950 (MI355X) only: 64-lane wavefronts, bf16 MFMA 32x32x16.
 #pragma once
 
@@ -64,6 +66,8 @@ struct AttnArgs {
   float* lse2;            // [total_q][64] log2 domain, nullable (n_split == 1)
   float v_scale;          // output factor (the V scale of FP8 storage; 1 otherwise)
   int32_t direct;         // q-tile kernel with n_split == 1: write out/lse itself (no partials)
+  int32_t* plan_miss;     // work-list launches: [total_q], 1 if query i's keys run past its
+                          // planned splits (written by the last planned split), else 0
 };
 
 // (query, split) pairs of a launch in launch order: workgroup b takes item b, so that the
@@ -74,17 +78,6 @@ struct WorkList {
   int32_t n;
   uint32_t item[kMaxWorkItems];  // query << 9 | split (split < 512)
 };
-
-__device__ inline void work_item(const WorkList& wl, int n_split, int& i, int& split) {
-  if (wl.n > 0) {
-    const uint32_t it = wl.item[blockIdx.x];
-    i = (int)(it >> 9);
-    split = (int)(it & 511u);
-  } else {
-    i = blockIdx.x / n_split;
-    split = blockIdx.x - i * n_split;
-  }
-}
 
 struct CombineArgs {
   SeqsDev b;
@@ -100,6 +93,7 @@ struct CombineArgs {
   uint32_t* hist;         // nullable: [total_q][kHistBins] zeroed here for the score pass
   uint32_t* counters;     // nullable: [total_q][4] zeroed here
   float v_scale;          // output factor (the V scale of FP8 storage; 1 otherwise)
+  const int32_t* plan_miss;  // nullable: the attention launch's plan-miss flags
 };
 
 struct ScoreArgs {
@@ -115,6 +109,7 @@ struct ScoreArgs {
   int64_t score_stride;   // floats per query in `scores`
   float* scores;          // [total_q][score_stride]
   uint32_t* hist;         // [total_q][kHistBins]
+  int32_t* plan_miss;     // work-list launches: [total_q] plan-miss flags of the score pass
 };
 
 struct TopkArgs {
@@ -131,6 +126,11 @@ struct TopkArgs {
   uint2* cand;            // [total_q][kCandCap]: (score bits, position)
   int32_t* sel_idx;       // [total_q][top_k]
   int32_t* sel_count;     // nullable
+  const int32_t* miss_attn;   // nullable: plan-miss flags of the attention launch
+  const int32_t* miss_score;  // nullable: plan-miss flags of the score launch
+  void* out;              // with the flags: outputs of a missed query are set to NaN
+  float* lse;             // nullable
+  int32_t out_f32;        // out holds fp32 (else bf16)
 };
 
 struct BridgeArgs {
@@ -157,56 +157,6 @@ struct AppendArgs {
   int32_t n_mats;
   int32_t n_slices;        // d_model / kAppendSlice
 };
-
-// Resolves query i: sequence row base and position t. Returns false when the
-// descriptor is inconsistent (the query is then not computed), which includes a position
-// at or beyond max_kv_len: the key splits and score rows are sized from that bound. The sequence is first
-// guessed proportionally (exact for batches with equal query counts per sequence), and
-// found by binary search over q_start otherwise.
-__device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t) {
-  int lo = (int)(((int64_t)i * b.num_seqs) / max(1, b.total_q));
-  if (lo >= b.num_seqs) lo = b.num_seqs - 1;
-  if (!(b.q_start[lo] <= i && i < b.q_start[lo + 1])) {
-    lo = 0;
-    int hi = b.num_seqs - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (b.q_start[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-  }
-  base = b.kv_start[lo];
-  const int n = b.kv_len[lo];
-  t = b.q_pos[i];
-  const bool ok = b.q_start[lo] <= i && i < b.q_start[lo + 1] && t >= 0 && t < n && t < b.max_kv_len &&
-                  base >= 0 && base + (int64_t)n <= b.total_rows;
-  if (!ok) { base = 0; t = 0; }
-  return ok;
-}
-
-// One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane l's
-// 16 bytes land at LDS byte address `lds` + 16*l (`lds` must be wave-uniform). Issued as
-// asm so that the wait for it can be placed by hand with s_waitcnt vmcnt (the compiler
-// otherwise waits for every pending LDS copy before any LDS read). The asm has no
-// register results; M0, which holds the LDS address, is saved and restored around it.
-__device__ inline void dma16(const void* g, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0\n"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds)
-      : "memory");
-}
-
-// Number of logical keys of a query: t+1 (full causal) or top_k + min(window, t+1)
-// (gather: selected slots first, then the window rows oldest first).
-__device__ inline int logical_keys(bool gather, int t, int window, int top_k) {
-  return gather ? top_k + min(window, t + 1) : t + 1;
-}
 
 // ---------------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).

@@ -58,14 +58,16 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
   work_item(wl, a.n_split, i, split);
   int64_t base;
   int t;
-  if (!__builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t))) return;
+  const bool valid = __builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t));
   // the descriptor is the same on every lane (query i): keep the loop control scalar
   t = __builtin_amdgcn_readfirstlane(t);
   base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
                    (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
   const int nc = max(0, t - a.window + 1);
-  if (nc <= a.top_k) return;
   const int k0 = split * a.split_keys;
+  if (wl.n > 0 && a.plan_miss != nullptr && threadIdx.x == 0 && last_planned(wl, i))
+    a.plan_miss[i] = (valid && nc > a.top_k && k0 + a.split_keys < nc) ? 1 : 0;
+  if (!valid || nc <= a.top_k) return;
   if (k0 >= nc) return;
   const int k1 = min(nc, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;

@@ -20,7 +20,7 @@
 //           candidates in LDS (or, if b1 overflowed the list, by streaming the query's
 //           scores again), then order the k positions ascending and write them.
 //           Queries with at most k candidates take all of them.
-#include "hs2_internal.h"
+#include "kernel_common.h"
 
 namespace hs2 {
 namespace {
@@ -88,6 +88,12 @@ __device__ inline void threshold_bin(const uint32_t* __restrict__ hist, int k, u
 }
 
 __device__ inline int cand_count(int t, int window) { return max(0, t - window + 1); }
+
+// True if the attention or score launch of query i was planned from host lengths that
+// its device length exceeds (see last_planned): its partials or scores are incomplete.
+__device__ inline bool plan_missed(const TopkArgs& a, int i) {
+  return (a.miss_attn != nullptr && a.miss_attn[i] != 0) || (a.miss_score != nullptr && a.miss_score[i] != 0);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ inline uint32_t wave_incl_scan(uint32_t x) {
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
   const int split = blockIdx.x - i * a.n_split;
   int64_t base;
   int t;
-  if (!query_desc(a.b, i, base, t)) return;
+  if (!query_desc(a.b, i, base, t) || plan_missed(a, i)) return;
   const int nc = cand_count(t, a.window);
   if (a.top_k == 0 || nc <= a.top_k) return;
   filter_chunk(a, i, nc, split, s_wave, s_res, s_tot);
@@ -404,10 +410,19 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
   int64_t base;
   int t;
   const int k = a.top_k;
-  if (!query_desc(a.b, i, base, t)) {
+  const bool valid = query_desc(a.b, i, base, t);
+  if (!valid || plan_missed(a, i)) {
     if (out)
       for (int e = threadIdx.x; e < k; e += kThreads) out[e] = -1;
     if (a.sel_count && threadIdx.x == 0) a.sel_count[i] = -1;
+    if (valid) {  // a missed plan: the query's outputs are not computed either
+      const size_t o0 = (size_t)i * kHeads * kDim;
+      for (int e = threadIdx.x; e < kHeads * kDim; e += kThreads) {
+        if (a.out_f32) static_cast<float*>(a.out)[o0 + e] = NAN;
+        else static_cast<__bf16*>(a.out)[o0 + e] = (__bf16)NAN;
+      }
+      if (a.lse && threadIdx.x < kHeads) a.lse[(size_t)i * kHeads + threadIdx.x] = NAN;
+    }
     return;
   }
   const int nc = cand_count(t, a.window);

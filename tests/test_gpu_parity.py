@@ -1,8 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Small cases are checked on every output element; the five workloads at full size
-are checked on sampled queries (every output of a sampled query) plus properties
-that hold for every query (counts, ordering, planted needles).
+are checked element by element on every query of the decode batches (64 x 128k in
+bf16 and FP8, 8 x 1M, the 32 ragged sequences) and on 72 queries of the 4,096-query
+chunk, plus properties that hold for every query (counts, ordering, planted needles).
 """
 import math
 
@@ -281,6 +282,98 @@ def test_position_beyond_max_kv_len_is_not_computed():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_host_lengths_below_device_lengths_are_reported(dtype):
+    """The decode launches are planned from the host copy of the lengths (kv_len_host).
+    A sequence whose device length exceeds its host copy has key splits that were never
+    launched: its query is reported as inconsistent (NaN outputs, sel_count -1), also
+    with a host length of 0; a host length above the device length only over-covers.
+    Nothing is written past the workspaces; the other queries match the oracle."""
+    lens = [50000 + 997 * j for j in range(8)]
+    spec = BlockSpec("host-lengths", lens, [[n - 1] for n in lens], dtype=dtype, n_sparse=1,
+                     needles_per_query=2, seed=41)
+    inp = make_block_inputs(spec)
+    dev = "cuda"
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, dev)
+    host = batch.kv_len_host.copy()
+    host[3] = 1000           # far below the device length: most splits of query 3 are missing
+    host[5] = 0              # nothing planned: one split is still launched, and it reports
+    host[6] = min(batch.max_kv_len, int(host[6]) + 3000)   # above the device length
+    batch.kv_len_host = np.ascontiguousarray(host, dtype=np.int32)
+    fp8 = dtype == "fp8"
+    k, v, q, qs = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q_sel), to_dev(inp.q_sp[0])
+    ws_dt = "fp8" if fp8 else torch.bfloat16
+    guard = 1 << 16
+    n1 = hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k, ws_dt)
+    n2 = max(1, hs2.sparse_attn_workspace_size(batch, spec.window, spec.top_k, ws_dt))
+    ws1 = torch.full((n1 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    ws2 = torch.full((n2 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    _say(f"host lengths below device lengths ({dtype})")
+    if fp8:
+        out, lse, sel, cnt = hs2.full_attn_select_fp8kv(batch, q, k, v, spec.k_scale, spec.v_scale, spec.window,
+                                                        spec.top_k, spec.scale, workspace=ws1[:n1])
+        o, _ = hs2.sparse_attn_fp8kv(batch, qs, k, v, spec.k_scale, spec.v_scale, sel, spec.window, spec.top_k,
+                                     spec.scale, workspace=ws2[:n2])
+    else:
+        out, lse, sel, cnt = hs2.full_attn_select(batch, q, k, v, spec.window, spec.top_k, spec.scale,
+                                                  workspace=ws1[:n1])
+        o, _ = hs2.sparse_attn(batch, qs, k, v, sel, spec.window, spec.top_k, spec.scale, workspace=ws2[:n2])
+    torch.cuda.synchronize()
+    assert bool((ws1[n1:] == 0x5A).all()) and bool((ws2[n2:] == 0x5A).all())
+    g_out, g_lse, g_sel, g_cnt, g_sp = from_dev(out), from_dev(lse), sel.cpu().numpy(), cnt.cpu().numpy(), from_dev(o)
+    rr = fp8
+    for qi in (3, 5):
+        assert int(g_cnt[qi]) == -1 and np.all(g_sel[qi] == -1), f"query {qi}: selection not reported"
+        assert np.isnan(g_out[qi]).all() and np.isnan(g_lse[qi]).all(), f"query {qi}: outputs not NaN"
+        # the sparse layer's own descriptor is consistent: with an all -1 selection it
+        # attends the window alone
+        ref, _ = oracle_sparse(inp, qi, 0, g_sel[qi])
+        check_attn(g_sp[qi], ref, f"host lengths {dtype} q{qi} sparse layer, window only", beyond_rounding=rr)
+    for qi in (0, 6, 7):
+        r = oracle_query(inp, qi)
+        tag = f"host lengths {dtype} q{qi}"
+        check_attn(g_out[qi], r["out"], tag, beyond_rounding=rr)
+        check_lse(g_lse[qi], r["lse"], tag)
+        check_selection(g_sel[qi], int(g_cnt[qi]), r, spec.top_k, oracle.candidate_count(r["t"], spec.window), tag)
+        ref, _ = oracle_sparse(inp, qi, 0, g_sel[qi], r["K"], r["V"])
+        check_attn(g_sp[qi], ref, tag + " sparse layer", beyond_rounding=rr)
+
+
+def test_q_start_beyond_total_q_touches_nothing_outside():
+    """Q-tile path (many queries per sequence): a q_start that runs past total_q, or that
+    starts below 0, makes every query inconsistent (NaN outputs, sel_count -1) and no
+    kernel touches a row past the caller's Q, out, LSE, selection or workspace buffers."""
+    spec = BlockSpec("qstart", [6000, 9000], [list(range(5988, 6000)), list(range(8992, 9000))], dtype="bf16",
+                     n_sparse=0, needles_per_query=0, seed=43)
+    inp = make_block_inputs(spec)
+    dev = "cuda"
+    nq = spec.total_q
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    extra = 48   # rows of every per-query buffer past total_q, filled with a guard pattern
+    q = torch.zeros(nq + extra, 64, 128, dtype=torch.bfloat16, device=dev)
+    q[:nq] = to_dev(inp.q_sel)
+    for bad in ([0, 12, 40], [-8, 12, 20]):
+        batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, dev)
+        assert batch.max_q_per_seq >= 8  # the q-tile kernels
+        batch.q_start = torch.tensor(bad, dtype=torch.int32, device=dev)
+        out = torch.full((nq + extra, 64, 128), 3.0, dtype=torch.bfloat16, device=dev)
+        lse = torch.full((nq + extra, 64), 3.0, dtype=torch.float32, device=dev)
+        sel = torch.full((nq + extra, spec.top_k), 7, dtype=torch.int32, device=dev)
+        cnt = torch.full((nq + extra,), 7, dtype=torch.int32, device=dev)
+        n1 = hs2.full_attn_select_workspace_size(batch, spec.window, spec.top_k)
+        guard = 1 << 16
+        ws = torch.full((n1 + guard,), 0x5A, dtype=torch.uint8, device=dev)
+        _say(f"q_start {bad}")
+        hs2.full_attn_select(batch, q[:nq], k, v, spec.window, spec.top_k, spec.scale, out=out[:nq], lse=lse[:nq],
+                             sel_idx=sel[:nq], sel_count=cnt[:nq], workspace=ws[:n1])
+        torch.cuda.synchronize()
+        assert bool((ws[n1:] == 0x5A).all()), "workspace guard bytes changed"
+        assert bool((out[nq:].float() == 3.0).all()) and bool((lse[nq:] == 3.0).all())
+        assert bool((sel[nq:] == 7).all()) and bool((cnt[nq:] == 7).all())
+        assert bool(torch.isnan(out[:nq].float()).all()) and bool(torch.isnan(lse[:nq]).all())
+        assert bool((cnt[:nq] == -1).all()) and bool((sel[:nq] == -1).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_repeat_runs_are_bitwise_identical(dtype):
     inp = make_block_inputs(BlockSpec("det", [20000, 7000], [[19999], [6999, 3000]], dtype=dtype, n_sparse=1,
                                       needles_per_query=4, seed=18))
@@ -507,19 +600,21 @@ def _full(n, sample):
 
 
 def test_workload2_decode_64x128k():
-    _full(2, [0, 37, 63])
+    _full(2, range(64))
 
 
 def test_workload3_decode_8x1m():
-    _full(3, [0, 7])
+    _full(3, range(8))
 
 
 def test_workload6_decode_64x128k_fp8():
-    _full(6, [0, 41, 63])
+    _full(6, range(64))
 
 
 def test_workload4_chunk_4096_queries():
-    _full(4, [0, 2048, 4095])
+    # every wave (query index mod 8) of q-tiles spread over the chunk, the first and the
+    # last tile included; each query's candidates span several score splits of 32,768 keys
+    _full(4, [8 * tile + w for tile in list(range(0, 512, 64)) + [511] for w in range(8)])
 
 
 def test_workload5_bridge_and_ragged_decode():
@@ -533,7 +628,7 @@ def test_workload5_bridge_and_ragged_decode():
     _bridge_check(bi, gk, gv, rows)
     del h, gk, gv
     torch.cuda.empty_cache()
-    _full(5, [0, 13, 31])
+    _full(5, range(32))
 
 
 @pytest.mark.parametrize("shape", ["decode", "chunk", "decode-fp8"])
