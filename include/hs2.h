@@ -194,6 +194,24 @@ hs2_status hs2_sparse_attn(const hs2_seqs* batch, const void* q, const void* k, 
                            void* workspace, size_t workspace_bytes, hs2_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * hs2_sparse_attn for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same operation and
+ * arguments as hs2_sparse_attn (dt HS2_BF16 or HS2_F32), without a workspace: the split
+ * partials live in a device array of HS2_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends (no memory is allocated by the call). A
+ * batch whose hs2_sparse_attn_workspace_size exceeds HS2_NOALLOC_SCRATCH_BYTES returns
+ * HS2_ERR_WORKSPACE. The stream must belong to the current device (HS2_ERR_INVALID_ARG
+ * otherwise). Calls on one GPU share its array: calls that overlap there (other streams or
+ * threads) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------------------ */
+#define HS2_NOALLOC_SCRATCH_BYTES (16u << 20) /* 16 MiB per GPU: e.g. 64 queries x 7 splits */
+
+hs2_status hs2_sparse_attn_noalloc(const hs2_seqs* batch, const void* q, const void* k, const void* v,
+                                   const int32_t* sel_idx, int32_t n_heads, int32_t head_dim,
+                                   int32_t window, int32_t top_k, float scale, void* out, float* lse,
+                                   hs2_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Decode-time KV Bridging ([arex] "Outer KV Bridging, inner KV Reuse"): in decode each
  * new token's hidden state h_i (the input of the matching self-decoder full-attention
  * layer) goes through every bridged layer's own projections, and the results become

@@ -33,6 +33,17 @@ hs2_status ok() {
   return HS2_OK;
 }
 
+}  // namespace
+
+namespace hs2 {
+hs2_status set_error(hs2_status st, const char* msg) {
+  g_err = msg;
+  return st;
+}
+}  // namespace hs2
+
+namespace {
+
 constexpr size_t kAlign = 256;
 constexpr int kTargetGroups = 256;  // workgroups per launch: one per CU
 constexpr int kMaxSplit = 256;      // bound of the split combine
@@ -488,15 +499,30 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   return ok();
 }
 
-hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, const void* v, float k_scale,
-                       float v_scale, const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
-                       int32_t top_k, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                       hs2_dtype dt, void* stream) {
+}  // namespace
+
+namespace hs2 {
+// Every argument check of a sparse-layer call except the workspace's.
+hs2_status sparse_check(const hs2_seqs* batch, const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                        int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k, float scale,
+                        const void* out, const float* lse, hs2_dtype dt) {
   hs2_status st = check_attn_common(batch, q, k, v, n_heads, head_dim, window, top_k, scale, out, lse, dt);
   if (st != HS2_OK) return st;
   if (top_k > 0 && batch->total_q > 0 && !sel_idx)
     return fail(HS2_ERR_INVALID_ARG, "sel_idx must not be NULL when top_k > 0");
   if (sel_idx && !aligned(sel_idx, 4)) return fail(HS2_ERR_INVALID_ARG, "sel_idx must be 4-byte aligned");
+  return HS2_OK;
+}
+}  // namespace hs2
+
+namespace {
+
+hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, const void* v, float k_scale,
+                       float v_scale, const int32_t* sel_idx, int32_t n_heads, int32_t head_dim, int32_t window,
+                       int32_t top_k, float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hs2_dtype dt, void* stream) {
+  hs2_status st = sparse_check(batch, q, k, v, sel_idx, n_heads, head_dim, window, top_k, scale, out, lse, dt);
+  if (st != HS2_OK) return st;
   const SparsePlan p = plan_sparse(batch, window, top_k);
   if (workspace_bytes < p.total || (p.total > 0 && !workspace))
     return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,

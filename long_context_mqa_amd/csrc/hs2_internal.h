@@ -158,6 +158,15 @@ struct AppendArgs {
   int32_t n_slices;        // d_model / kAppendSlice
 };
 
+// Sets the calling thread's hs2_last_error() text and returns st (for entry points
+// defined outside hs2_api.cpp).
+hs2_status set_error(hs2_status st, const char* msg);
+
+// Every argument check of hs2_sparse_attn except the workspace's (sets hs2_last_error).
+hs2_status sparse_check(const hs2_seqs* batch, const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                        int32_t n_heads, int32_t head_dim, int32_t window, int32_t top_k, float scale,
+                        const void* out, const float* lse, hs2_dtype dt);
+
 // ---------------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------------

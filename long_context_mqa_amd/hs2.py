@@ -31,6 +31,7 @@ EXPORTED = [
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
     "hs2_sparse_attn",
+    "hs2_sparse_attn_noalloc",
     "hs2_bridge_kv_append_workspace_size",
     "hs2_bridge_kv_append",
     "hs2_causal_attn_workspace_size",
@@ -95,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_sparse_attn_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_sparse_attn.restype = I32
     lib.hs2_sparse_attn.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, I32, P]
+    lib.hs2_sparse_attn_noalloc.restype = I32
+    lib.hs2_sparse_attn_noalloc.argtypes = [SP, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P]
     lib.hs2_bridge_kv_append_workspace_size.restype = SZ
     lib.hs2_bridge_kv_append_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hs2_bridge_kv_append.restype = I32
@@ -255,6 +258,27 @@ def sparse_attn(batch: Batch, q, k, v, sel_idx, window: int = 128, top_k: int | 
     _check(lib.hs2_sparse_attn(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx) if top_k > 0 else None,
                                q.shape[1], q.shape[2], window, top_k, scale, _ptr(out), _ptr(lse), _ptr(workspace),
                                workspace.numel(), dt, _stream(stream)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sparse_attn_noalloc(batch: Batch, q, k, v, sel_idx, window: int = 128, top_k: int | None = None,
+                        scale: float | None = None, out=None, lse=None, stream=None):
+    """hs2_sparse_attn_noalloc: the sparse layer with its split partials in the library's
+    fixed per-GPU scratch array (no workspace argument). Returns (out, lse)."""
+    lib = load()
+    dt = _dtype_code(q)
+    if top_k is None:
+        top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    b = batch.c()
+    _check(lib.hs2_sparse_attn_noalloc(ctypes.byref(b), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(sel_idx) if top_k > 0 else None, q.shape[1], q.shape[2], window, top_k,
+                                       scale, _ptr(out), _ptr(lse), dt, _stream(stream)))
     return out, lse
 
 

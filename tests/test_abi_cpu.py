@@ -299,3 +299,23 @@ def test_header_is_plain_c99_and_a_c_program_links(lib, tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "num_seqs" in r.stdout
+
+
+def test_noalloc_rejects_a_batch_beyond_its_scratch(lib):
+    """hs2_sparse_attn_noalloc refuses, on the host, a batch whose workspace exceeds the
+    fixed scratch array (a wide window splits every query's keys over many workgroups),
+    and takes only bf16 or fp32 K/V."""
+    b = _batch(total_q=100, max_kv_len=300000, rows=30000000, num_seqs=100)
+    window, top_k = 1 << 18, 4096
+    need = lib.hs2_sparse_attn_workspace_size(ctypes.byref(b), 64, 128, window, top_k, hs2.HS2_BF16)
+    assert need > hs2.NOALLOC_SCRATCH_BYTES
+    st = lib.hs2_sparse_attn_noalloc(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE * 3, 64, 128, window, top_k, 0.088,
+                                     FAKE * 2, None, hs2.HS2_BF16, None)
+    assert st == hs2.HS2_ERR_WORKSPACE
+    assert b"scratch" in lib.hs2_last_error()
+    st = lib.hs2_sparse_attn_noalloc(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE * 3, 64, 128, 128, 1024, 0.088,
+                                     FAKE * 2, None, hs2.HS2_FP8_E4M3, None)
+    assert st == hs2.HS2_ERR_UNSUPPORTED
+    st = lib.hs2_sparse_attn_noalloc(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE * 3, 32, 128, 128, 1024, 0.088,
+                                     FAKE * 2, None, hs2.HS2_BF16, None)
+    assert st == hs2.HS2_ERR_UNSUPPORTED
