@@ -31,6 +31,7 @@
 // values, so the output is an exactly normalised average of V rows; the LSE uses the sum
 // of the unrounded values.
 #include "attn_decode.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

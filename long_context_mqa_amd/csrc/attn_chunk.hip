@@ -20,6 +20,7 @@
 // This file is built with the MFMA results in VGPRs (no accumulator registers): both
 // kernels stay within 256 registers, the budget of two waves per SIMD.
 #include "attn_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

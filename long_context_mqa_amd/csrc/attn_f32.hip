@@ -11,6 +11,7 @@
 // Thread layout: 256 threads = 64 heads x 4 slices of 32 dims. A logit is the sum of the
 // four slice dot products (two xor-shuffles within the four lanes of a head).
 #include "kernel_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

@@ -10,6 +10,7 @@
 // publishes the MiMo-V3 core architecture HySparse2", section "Numbers computed on three
 // 80B-A3B models": the KV cache is accounted in FP8.
 #include "attn_decode.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 

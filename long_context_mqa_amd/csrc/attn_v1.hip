@@ -29,6 +29,7 @@
 // is needed for block-level selection.
 #include "attn_common.h"
 #include "v1_internal.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

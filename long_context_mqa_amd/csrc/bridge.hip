@@ -22,6 +22,7 @@
 // Tiles of the same rows run back to back on one XCD, so H is read from HBM once and
 // re-served from that XCD's L2 for the other column tiles.
 #include "kernel_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

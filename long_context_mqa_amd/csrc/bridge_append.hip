@@ -17,6 +17,7 @@
 // out^T = W^T H^T with W^T as the A operand and H^T as the B operand in the same
 // permuted contraction order as the P^T operand of O^T += V^T P^T.
 #include "attn_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

@@ -8,8 +8,7 @@
 #include <string>
 
 #include "hs2.h"
-#include "hs2_internal.h"
-#include "v1_internal.h"
+#include "hs2_launch.h"
 
 
 namespace {

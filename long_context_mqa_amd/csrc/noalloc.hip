@@ -11,7 +11,7 @@
 // call relies on (every partial the combine reads is written first by the same call).
 #include <mutex>
 
-#include "hs2_internal.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

@@ -8,6 +8,7 @@
 // Built with the MFMA results in VGPRs (no accumulator registers): the loop needs about
 // 180 registers, and the softmax reads every result element once per tile.
 #include "attn_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

@@ -21,6 +21,7 @@
 //           scores again), then order the k positions ascending and write them.
 //           Queries with at most k candidates take all of them.
 #include "kernel_common.h"
+#include "hs2_launch.h"
 
 namespace hs2 {
 namespace {

@@ -67,8 +67,4 @@ struct V1GateArgs {
   __bf16* out;               // [total_q][64][128]
 };
 
-hipError_t launch_v1_attn(const V1AttnArgs& a, bool sparse, int grid, hipStream_t s);
-hipError_t launch_v1_select(const V1SelectArgs& a, hipStream_t s);
-hipError_t launch_v1_gate(const V1GateArgs& a, hipStream_t s);
-
 }  // namespace hs2

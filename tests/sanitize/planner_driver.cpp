@@ -16,8 +16,7 @@
 #include <vector>
 
 #include "hs2.h"
-#include "hs2_internal.h"
-#include "v1_internal.h"
+#include "hs2_launch.h"
 
 namespace {
 
