@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhs2.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_chunk.hip", "score_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "bridge_append.hip", "attn_v1.hip", "noalloc.hip",
+SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_chunk.hip", "score_bf16.hip", "attn_f32.hip", "topk.hip", "bridge.hip", "bridge_append.hip", "attn_v1.hip", "noalloc.hip", "sparse_attn.hip",
            "hs2_api.cpp"]
 # Kernels whose MFMA results are consumed element by element every tile and that fit in
 # the 256 VGPRs: MFMA destinations in VGPRs instead of accumulator registers (AGPRs),

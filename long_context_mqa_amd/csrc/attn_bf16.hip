@@ -1,7 +1,7 @@
-// bf16 MQA attention for gfx950: the selector's exact causal attention (pass 1) and the
-// sparse layers' gathered attention (the decode-shaped kernel of attn_decode.h with four
-// waves per workgroup), and the split combine. The selection-score pass is in
-// score_bf16.hip, the FP8 K/V instantiation in attn_fp8.hip.
+// bf16 MQA attention for gfx950: the selector's exact causal attention (pass 1, the
+// decode-shaped kernel of attn_decode.h with four waves per workgroup) and the split
+// combine (also used by the sparse layers of sparse_attn.hip). The selection-score pass is
+// in score_bf16.hip, the FP8 K/V instantiation in attn_fp8.hip.
 //
 // Method (page title and section):
 //   arex-research.com, "Xiaomi MiMo lead Luo Fuli publishes the MiMo-V3 core architecture
@@ -123,22 +123,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
-                            uint32_t* counters, hipStream_t s) {
-  if (gather)
-    hipLaunchKernelGGL((attn_bf16_kernel<KvBf16, true, 4>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<KvBf16, false, 4>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_fp8kv_full(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist,
-                                  uint32_t* counters, hipStream_t s);  // attn_fp8.hip
-
-hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
-                             uint32_t* counters, hipStream_t s) {
-  if (!gather) return launch_attn_fp8kv_full(a, wl, grid, hist, counters, s);
-  hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, true, 4>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
+hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist, uint32_t* counters,
+                            hipStream_t s) {
+  hipLaunchKernelGGL((attn_bf16_kernel<KvBf16, 4>), dim3(grid), dim3(256), 0, s, a, wl, hist, counters);
   return hipGetLastError();
 }
 

@@ -68,30 +68,15 @@ __device__ inline int v_chunk(int row, int pos) { return pos ^ ((row & 3) << 2);
 __device__ inline int k8_swz(int row) { return (row >> 1) & 7; }
 __device__ inline int v8_swz(int row) { return (row & 2) | ((row >> 1) & 4); }
 
-// Logical key list of one query. Full mode: positions 0..t. Gather mode: top_k selected
-// slots (entries outside the candidate range are masked) followed by the window rows.
+// Key list of one query in the selector's attention pass: positions 0 .. n_keys-1 (the
+// causal range 0..t) of the sequence whose first row is `base`.
 struct KeyList {
-  const int32_t* sel_lds;  // gather mode: selected rows of slots [sel_k0, ...) in LDS
-  int sel_k0;
   int64_t base;
-  int t, top_k, n_keys, w_eff, cand_hi;
-  bool gather;
+  int n_keys;
 
   __device__ inline void row(int p, int& rel, bool& ok) const {
-    if (!gather) {
-      ok = p < n_keys;
-      rel = ok ? p : 0;
-      return;
-    }
-    if (p < top_k) {
-      const int s = sel_lds[p - sel_k0];
-      ok = s >= 0 && s <= cand_hi;
-      rel = ok ? s : 0;
-      return;
-    }
-    const int w = p - top_k;
-    ok = w < w_eff;
-    rel = ok ? (t - w_eff + 1 + w) : 0;
+    ok = p < n_keys;
+    rel = ok ? p : 0;
   }
 };
 

@@ -1,7 +1,7 @@
 // The decode-shaped attention kernel (one query per workgroup): the selector's exact
-// causal attention (pass 1) and the sparse layers' gathered attention, templated on the
-// storage format of K/V and on the number of waves per workgroup (4 for bf16 tiles, 8
-// for FP8 tiles, whose smaller tiles need two waves per SIMD to keep the SIMD busy).
+// causal attention (pass 1), templated on the storage format of K/V and on the number of
+// waves per workgroup (4 for bf16 tiles, 8 for FP8 tiles, whose smaller tiles need two
+// waves per SIMD to keep the SIMD busy).
 // Included by attn_bf16.hip and attn_fp8.hip; the layout notes are in attn_bf16.hip.
 #pragma once
 
@@ -13,9 +13,7 @@ namespace {
 using namespace attn;
 
 // Shared memory of the attention kernel: per-wave K and V stages during the key loop,
-// then the cross-wave merge; Q (in MFMA operand order) and the gathered row list stay
-// outside the union.
-constexpr int kSelMax = 2048;  // gathered slots per workgroup (the host caps the split)
+// then the cross-wave merge; Q (in MFMA operand order) stays outside the union.
 constexpr int kStageArea = 131072;  // LDS of the K/V stages of a workgroup, split over its waves
 constexpr int kMergeWaves = 4;      // waves of the final merge (an 8-wave group folds 4-7 into 0-3 first)
 
@@ -41,7 +39,6 @@ struct AttnSmem {
     } mg;
   };
   uint8_t q[kHeads * kDim * 2];
-  int32_t sel[kSelMax];
 };
 
 // Streams the tiles ord.at(wave), ord.at(wave + kW), ... of the workgroup's key range
@@ -108,11 +105,10 @@ __device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem<kW>&
   stream_tail<Kv, kW, kMaxOnly, S - 1>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, ntw);
 }
 
-template <typename Kv, bool kGather, int kW>
+template <typename Kv, int kW>
 __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList wl, uint32_t* hist,
                                                            uint32_t* counters) {
   constexpr int kThreads = 64 * kW;
-  constexpr int kSelPerThread = kSelMax / kThreads;
   constexpr int kQPieces = kHeads * kDim * 2 / 16 / kThreads;  // 16-byte pieces of Q per thread
   __shared__ __align__(16) AttnSmem<kW> sm;
   const int lane = threadIdx.x & 63;
@@ -121,19 +117,8 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
   work_item(wl, a.n_split, i, split);
   const int k0 = split * a.split_keys;
 
-  // Loads that do not depend on the query's position go out first: the gathered slots
-  // of this split (gather mode: the key count exceeds top_k, so the slot range is known)
-  // and Q in MFMA operand order: 16-byte piece (nb, s, lane) = Q[32nb + l%32][(l/32)*64 + 8s ..]
-  int32_t selv[kSelPerThread];
-  const int s1 = kGather ? min(min(a.top_k, k0 + a.split_keys), k0 + kSelMax) : 0;
-  if (kGather) {
-    const int32_t* selr = a.sel + (size_t)i * a.top_k;
-#pragma unroll
-    for (int u = 0; u < kSelPerThread; ++u) {
-      const int p = k0 + (int)threadIdx.x + kThreads * u;
-      selv[u] = p < s1 ? selr[p] : -1;
-    }
-  }
+  // Q goes out before the descriptor is known, in MFMA operand order: 16-byte piece
+  // (nb, s, lane) = Q[32nb + l%32][(l/32)*64 + 8s ..]
   bf16x8 qv[kQPieces];
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)i * kHeads * kDim;
@@ -156,7 +141,7 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
     for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) hist[(size_t)i * kHistBins + e] = 0u;
     if (threadIdx.x < 4) counters[(size_t)i * 4 + threadIdx.x] = 0u;
   }
-  if (!kGather && wl.n > 0 && a.plan_miss != nullptr && threadIdx.x == 0 && last_planned(wl, i))
+  if (wl.n > 0 && a.plan_miss != nullptr && threadIdx.x == 0 && last_planned(wl, i))
     a.plan_miss[i] = (valid && k0 + a.split_keys < t + 1) ? 1 : 0;
   if (!valid) {
     if (a.n_split == 1) {
@@ -171,33 +156,18 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
   }
 
   KeyList kl;
-  kl.gather = kGather;
   kl.base = base;
-  kl.t = t;
-  kl.top_k = a.top_k;
-  kl.n_keys = logical_keys(kGather, t, a.window, a.top_k);
-  kl.w_eff = min(a.window, t + 1);
-  kl.cand_hi = t - a.window;
+  kl.n_keys = t + 1;
   if (k0 >= kl.n_keys) return;  // empty split: the combine does not read it
   const int k1 = min(kl.n_keys, k0 + a.split_keys);
   const int ntiles = (k1 - k0 + kTile - 1) / kTile;
-  kl.sel_lds = sm.sel;
-  kl.sel_k0 = k0;
-  if (kGather) {
-#pragma unroll
-    for (int u = 0; u < kSelPerThread; ++u) {
-      const int p = k0 + (int)threadIdx.x + kThreads * u;
-      if (p < s1) sm.sel[p - k0] = selv[u];
-    }
-  }
 #pragma unroll
   for (int u = 0; u < kQPieces; ++u) *reinterpret_cast<bf16x8*>(sm.q + ((int)threadIdx.x + kThreads * u) * 16) = qv[u];
   __syncthreads();
 
   const void* kp = a.k;
   const void* vp = a.v;
-  // the gathered rows of a sparse split are few and random: no rotation there
-  const TileOrder ord = kGather ? TileOrder{0, ntiles} : TileOrder::rotated(i * a.n_split + split, ntiles);
+  const TileOrder ord = TileOrder::rotated(i * a.n_split + split, ntiles);
   WaveState st;
   state_init(st);
   float mx[2] = {-INFINITY, -INFINITY};

@@ -14,12 +14,11 @@
 
 namespace hs2 {
 
-// The selector's pass 1 over an FP8 cache; the sparse layers' gathered FP8 attention (few
-// tiles per workgroup, bound by gather latency rather than by the per-tile chain) runs the
-// four-wave instantiation in attn_bf16.hip.
-hipError_t launch_attn_fp8kv_full(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist,
-                                  uint32_t* counters, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, false, 8>), dim3(grid), dim3(512), 0, s, a, wl, hist, counters);
+// The selector's pass 1 over an FP8 cache (the sparse layers' FP8 attention is in
+// sparse_attn.hip).
+hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist, uint32_t* counters,
+                             hipStream_t s) {
+  hipLaunchKernelGGL((attn_bf16_kernel<KvFp8, 8>), dim3(grid), dim3(512), 0, s, a, wl, hist, counters);
   return hipGetLastError();
 }
 

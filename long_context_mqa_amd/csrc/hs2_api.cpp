@@ -1,5 +1,6 @@
 // Host entry points of libhs2: argument checks, workspace planning and kernel launches.
 // Every check runs before anything is enqueued; the library allocates nothing.
+#include <algorithm>
 #include <cmath>
 #include <limits>
 #include <cstdarg>
@@ -209,14 +210,26 @@ struct SparsePlan {
   size_t total = 0;
 };
 
-SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k) {
+// bf16 and FP8 K/V: slices of whole tiles, at most sparse_slots() of them in LDS at once,
+// sized so that the launch holds about one workgroup per CU; fp32 K/V: key splits of the
+// fp32 gather kernel (at most kSparseSplitMax keys, the bound of its LDS row list).
+SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
   SparsePlan p;
   const int64_t tq = std::max(0, b->total_q);
   const int64_t max_keys = (int64_t)top_k + std::min<int64_t>(window, b->max_kv_len);
-  p.attn = plan_split(tq * max_keys, max_keys);
-  if (p.attn.split_keys > kSparseSplitMax) {  // gathered slots of a workgroup are staged in LDS
-    p.attn.split_keys = kSparseSplitMax;
-    p.attn.n_split = (int)ceil_div(max_keys, kSparseSplitMax);
+  if (dt == HS2_F32) {
+    p.attn = plan_split(tq * max_keys, max_keys);
+    if (p.attn.split_keys > kSparseSplitMax) {  // gathered slots of a workgroup are staged in LDS
+      p.attn.split_keys = kSparseSplitMax;
+      p.attn.n_split = (int)ceil_div(max_keys, kSparseSplitMax);
+    }
+  } else {
+    const int64_t tiles = std::max<int64_t>(1, ceil_div(max_keys, kTile));
+    int64_t per = std::min<int64_t>(ceil_div(std::max<int64_t>(1, tq) * tiles, kTargetGroups),
+                                    sparse_slots(dt == HS2_FP8_E4M3));
+    per = std::max<int64_t>({per, 1, ceil_div(tiles, kMaxSplit)});  // a very wide window: several batches
+    p.attn.split_keys = (int)(per * kTile);
+    p.attn.n_split = (int)ceil_div(tiles, per);
   }
   p.total = p.attn.n_split > 1 ? align_up((size_t)tq * p.attn.n_split * sizeof(Partial)) : 0;
   return p;
@@ -412,9 +425,9 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     else if (f32)
       e = launch_attn_f32(a, false, grid, hist, counters, s);
     else if (fp8)
-      e = launch_attn_fp8kv(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
+      e = launch_attn_fp8kv(a, p.attn_wl, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
     else
-      e = launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
+      e = launch_attn_bf16(a, p.attn_wl, p.attn_wl.n > 0 ? p.attn_wl.n : grid, hist, counters, s);
   }
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "full attention launch");
@@ -522,7 +535,7 @@ hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, cons
                        hs2_dtype dt, void* stream) {
   hs2_status st = sparse_check(batch, q, k, v, sel_idx, n_heads, head_dim, window, top_k, scale, out, lse, dt);
   if (st != HS2_OK) return st;
-  const SparsePlan p = plan_sparse(batch, window, top_k);
+  const SparsePlan p = plan_sparse(batch, window, top_k, dt);
   if (workspace_bytes < p.total || (p.total > 0 && !workspace))
     return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes,
                 p.total);
@@ -552,9 +565,7 @@ hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   LaunchMarks mk(s);
   hipError_t e = mk.before(0);
   if (e == hipSuccess)
-    e = f32   ? launch_attn_f32(a, true, grid, nullptr, nullptr, s)
-        : fp8 ? launch_attn_fp8kv(a, WorkList{}, true, grid, nullptr, nullptr, s)
-              : launch_attn_bf16(a, WorkList{}, true, grid, nullptr, nullptr, s);
+    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s) : launch_sparse_attn(a, fp8, grid, s);
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   if (p.attn.n_split > 1) {
@@ -630,7 +641,7 @@ hs2_status causal_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     else if (f32)
       e = launch_attn_f32(a, false, grid, nullptr, nullptr, s);
     else
-      e = launch_attn_bf16(a, p.attn_wl, false, p.attn_wl.n > 0 ? p.attn_wl.n : grid, nullptr, nullptr, s);
+      e = launch_attn_bf16(a, p.attn_wl, p.attn_wl.n > 0 ? p.attn_wl.n : grid, nullptr, nullptr, s);
   }
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "causal attention launch");
@@ -721,9 +732,8 @@ size_t hs2_sparse_attn_workspace_size(const hs2_seqs* batch, int32_t n_heads, in
                                       int32_t top_k, hs2_dtype dt) {
   (void)n_heads;
   (void)head_dim;
-  (void)dt;
   if (!batch || batch->total_q < 0 || batch->max_kv_len < 1 || window < 1 || top_k < 0) return 0;
-  return plan_sparse(batch, window, top_k).total;
+  return plan_sparse(batch, window, top_k, dt).total;
 }
 
 size_t hs2_bridge_kv_append_workspace_size(int32_t n_new, int32_t d_model, int32_t n_layers, int32_t head_dim) {

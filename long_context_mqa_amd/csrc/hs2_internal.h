@@ -22,6 +22,9 @@ constexpr int kHistShift = 31 - kHistBits;
 constexpr int kCandCap = 4096; // threshold-bin candidates kept per query for the in-LDS select
 constexpr int kQTile = 8;      // queries per q-tile of the chunked selector (one wave each)
 constexpr int kScoreSplitMax = 32768;  // keys per chunked score workgroup (16-bit LDS bin counts)
+constexpr int kSparseStageBytes = 147456;  // LDS of a sparse-layer workgroup's K/V tile slots
+// K/V tiles (32 rows each) a sparse-layer workgroup holds in LDS at once
+constexpr int sparse_slots(bool fp8) { return kSparseStageBytes / (2 * kTile * kDim * (fp8 ? 1 : 2)); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

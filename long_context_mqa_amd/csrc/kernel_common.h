@@ -29,32 +29,39 @@ __device__ inline bool last_planned(const WorkList& wl, int i) {
 
 // Resolves query i: sequence row base and position t. Returns false when the
 // descriptor is inconsistent (the query is then not computed), which includes a position
-// at or beyond max_kv_len: the key splits and score rows are sized from that bound. The sequence is first
-// guessed proportionally (exact for batches with equal query counts per sequence), and
-// found by binary search over q_start otherwise.
+// at or beyond max_kv_len: the key splits and score rows are sized from that bound. The
+// sequence is first guessed proportionally (exact for batches with equal query counts per
+// sequence) and every value of that guess is loaded at once, so that the common case
+// costs one round of loads; a wrong guess is corrected by binary search over q_start.
 __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t) {
   // the query index must name a row of Q, and q_start must run from 0 to total_q (a
   // q_start beyond total_q would otherwise map a kernel's query onto rows past the
   // caller's Q, out, LSE and selection buffers)
-  if (i < 0 || i >= b.total_q || b.q_start[0] != 0 || b.q_start[b.num_seqs] != b.total_q) {
+  if (i < 0 || i >= b.total_q) {
     base = 0;
     t = 0;
     return false;
   }
   int lo = (int)(((int64_t)i * b.num_seqs) / max(1, b.total_q));
   if (lo >= b.num_seqs) lo = b.num_seqs - 1;
-  if (!(b.q_start[lo] <= i && i < b.q_start[lo + 1])) {
+  const int qs0 = b.q_start[0], qsn = b.q_start[b.num_seqs];
+  int ql = b.q_start[lo], qh = b.q_start[lo + 1];
+  base = b.kv_start[lo];
+  int n = b.kv_len[lo];
+  t = b.q_pos[i];
+  if (!(ql <= i && i < qh)) {
     lo = 0;
     int hi = b.num_seqs - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
       if (b.q_start[mid] <= i) lo = mid; else hi = mid - 1;
     }
+    ql = b.q_start[lo];
+    qh = b.q_start[lo + 1];
+    base = b.kv_start[lo];
+    n = b.kv_len[lo];
   }
-  base = b.kv_start[lo];
-  const int n = b.kv_len[lo];
-  t = b.q_pos[i];
-  const bool ok = b.q_start[lo] <= i && i < b.q_start[lo + 1] && t >= 0 && t < n && t < b.max_kv_len &&
+  const bool ok = qs0 == 0 && qsn == b.total_q && ql <= i && i < qh && t >= 0 && t < n && t < b.max_kv_len &&
                   base >= 0 && base + (int64_t)n <= b.total_rows;
   if (!ok) { base = 0; t = 0; }
   return ok;

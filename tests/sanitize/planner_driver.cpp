@@ -84,19 +84,27 @@ static void attn_common(const AttnArgs& a, const WorkList& wl, bool gather, int 
   in_ws(a.plan_miss, (size_t)a.b.total_q * 4);
   if (wl.n > 0 && !gather) CHECK(a.plan_miss != nullptr);
 }
-hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
-                            uint32_t* counters, hipStream_t) {
-  attn_common(a, wl, gather, grid, hist, counters);
+hipError_t launch_attn_bf16(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist, uint32_t* counters,
+                            hipStream_t) {
+  attn_common(a, wl, false, grid, hist, counters);
   return hipSuccess;
 }
-hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, bool gather, int grid, uint32_t* hist,
-                             uint32_t* counters, hipStream_t) {
-  attn_common(a, wl, gather, grid, hist, counters);
+hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, int grid, uint32_t* hist, uint32_t* counters,
+                             hipStream_t) {
+  attn_common(a, wl, false, grid, hist, counters);
   return hipSuccess;
 }
 hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist, uint32_t* counters,
                            hipStream_t) {
   attn_common(a, WorkList{}, gather, grid, hist, counters);
+  return hipSuccess;
+}
+hipError_t launch_sparse_attn(const AttnArgs& a, bool, int grid, hipStream_t) {
+  ++g_launches;
+  CHECK(grid == a.b.total_q * a.n_split && a.split_keys % kTile == 0 && a.split_keys >= kTile);
+  CHECK(a.n_split <= 256 || a.split_keys > sparse_slots(false) * kTile);
+  if (a.n_split > 1) in_ws(a.part, part_bytes(a.b, a.n_split));
+  else CHECK(a.part == nullptr);
   return hipSuccess;
 }
 hipError_t launch_combine(const CombineArgs& a, bool, hipStream_t) {
