@@ -138,8 +138,10 @@ struct SelectPlan {
   Split attn, score;
   int f_split = 1, f_len = kFilterLen;
   int64_t score_stride = 0;
+  bool score_lists = false;  // decode-shaped bf16/FP8 score pass: candidate lists, not score rows
+  int list_waves = 0, list_cap = 0;
   size_t off_part = 0, off_lse2 = 0, off_scores = 0, off_hist = 0, off_counters = 0,
-         off_above = 0, off_cand = 0, off_miss = 0, total = 0;
+         off_above = 0, off_cand = 0, off_miss = 0, off_lists = 0, off_lcount = 0, off_lthr = 0, total = 0;
   bool lists() const { return attn_wl.n > 0 || score_wl.n > 0; }
 };
 
@@ -194,8 +196,22 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt, b
     off += align_up((size_t)2 * tq * sizeof(int32_t));
   }
   if (top_k > 0) {
-    p.off_scores = off;
-    off += align_up((size_t)tq * p.score_stride * sizeof(float));
+    p.score_lists = !p.chunk && dt != HS2_F32;
+    if (p.score_lists) {
+      // per (query, score split, wave): up to all of the wave's candidates as 8-byte pairs
+      p.list_waves = dt == HS2_FP8_E4M3 ? 8 : 4;
+      p.list_cap = (int)(ceil_div(ceil_div(p.score.split_keys, kTile), p.list_waves) * kTile);
+      const size_t nl = (size_t)tq * p.score.n_split * p.list_waves;
+      p.off_lists = off;
+      off += align_up(nl * p.list_cap * sizeof(uint2));
+      p.off_lcount = off;
+      off += align_up(nl * sizeof(int32_t));
+      p.off_lthr = off;
+      off += align_up((size_t)tq * p.score.n_split * sizeof(int32_t));
+    } else {
+      p.off_scores = off;
+      off += align_up((size_t)tq * p.score_stride * sizeof(float));
+    }
     p.off_above = off;
     off += align_up((size_t)tq * top_k * sizeof(int32_t));
     p.off_cand = off;
@@ -459,7 +475,16 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   tk.n_split = p.f_split;
   tk.split_len = p.f_len;
   tk.score_stride = p.score_stride;
-  tk.scores = top_k > 0 ? at<float>(workspace, p.off_scores) : nullptr;
+  tk.scores = top_k > 0 && !p.score_lists ? at<float>(workspace, p.off_scores) : nullptr;
+  if (top_k > 0 && p.score_lists) {
+    tk.lists = at<uint2>(workspace, p.off_lists);
+    tk.list_count = at<int32_t>(workspace, p.off_lcount);
+    tk.list_thr = at<int32_t>(workspace, p.off_lthr);
+    tk.list_cap = p.list_cap;
+    tk.list_waves = p.list_waves;
+    tk.list_splits = p.score.n_split;
+    tk.list_split_keys = p.score.split_keys;
+  }
   tk.hist = hist;
   tk.counters = counters;
   tk.above = top_k > 0 ? at<int32_t>(workspace, p.off_above) : nullptr;
@@ -483,7 +508,11 @@ hs2_status select_impl(const hs2_seqs* batch, const void* q, const void* k, cons
     sc.n_split = p.score.n_split;
     sc.split_keys = p.score.split_keys;
     sc.score_stride = p.score_stride;
-    sc.scores = at<float>(workspace, p.off_scores);
+    sc.scores = tk.scores ? const_cast<float*>(tk.scores) : nullptr;
+    sc.lists = const_cast<uint2*>(tk.lists);
+    sc.list_count = const_cast<int32_t*>(tk.list_count);
+    sc.list_thr = const_cast<int32_t*>(tk.list_thr);
+    sc.list_cap = tk.list_cap;
     sc.hist = hist;
     sc.plan_miss = tk.miss_score ? miss + tq : nullptr;
     e = mk.before(2);

@@ -110,9 +110,14 @@ struct ScoreArgs {
   int32_t n_split;
   int32_t split_keys;
   int64_t score_stride;   // floats per query in `scores`
-  float* scores;          // [total_q][score_stride]
+  float* scores;          // q-tile and fp32 kernels: [total_q][score_stride]
   uint32_t* hist;         // [total_q][kHistBins]
   int32_t* plan_miss;     // work-list launches: [total_q] plan-miss flags of the score pass
+  // decode-shaped bf16 and FP8 kernels: candidate lists instead of score rows
+  uint2* lists;           // [total_q][n_split][waves][list_cap]: (score bits, position)
+  int32_t* list_count;    // [total_q][n_split][waves]: entries of each list
+  int32_t* list_thr;      // [total_q][n_split]: the split's final threshold (first digit)
+  int32_t list_cap;
 };
 
 struct TopkArgs {
@@ -122,7 +127,14 @@ struct TopkArgs {
   int32_t n_split;        // filter workgroups per query
   int32_t split_len;      // candidates per filter workgroup
   int64_t score_stride;
-  const float* scores;
+  const float* scores;    // score rows (null when the score pass wrote candidate lists)
+  const uint2* lists;     // candidate lists of the score pass (see ScoreArgs), or null
+  const int32_t* list_count;
+  const int32_t* list_thr;
+  int32_t list_cap;
+  int32_t list_waves;     // lists per score split
+  int32_t list_splits;    // score splits per query
+  int32_t list_split_keys;  // candidates per score split
   const uint32_t* hist;
   uint32_t* counters;     // [total_q][4]: 0 = above count, 1 = threshold-bin count
   int32_t* above;         // [total_q][top_k]

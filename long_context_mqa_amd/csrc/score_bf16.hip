@@ -17,7 +17,8 @@ using namespace attn;
 
 // ------------------------------------------------------------------------------------
 // Selection score pass: score_j = sum_h exp2(x_hj - lse2_h) for candidates j <= t-window,
-// written per query, plus a histogram of the first radix digit (bits 30..19).
+// kept only where it can still be among the query's top k (see the lists below), plus a
+// histogram of the first radix digit (bits 30..19) of the kept scores.
 // S = Q K^T here (heads as rows): each lane sums its 32 head values of one key, and one
 // exchange with lane l^32 completes the 64-head sum. K tiles stream through kScoreStages
 // per-wave LDS stages (same swizzled layout and DMA as pass 1): 4 of bf16 tiles or 8 of
@@ -46,6 +47,34 @@ struct ScoreSmem {
   uint32_t hist[kHistBins];
   float sbuf[kSWaves][kSFlush * kTile];
 };
+
+// The largest histogram bin b with count(bins >= b) >= k (the bin of the k-th largest
+// counted element), or 0 if the histogram holds fewer than k. One wave: lane l first sums
+// bins 64l .. 64l+63 (read in a rotated order, so that the 64 lanes hit 64 banks), then
+// the row found is searched bin by bin. Counts still being added by other waves only lower
+// the result.
+__device__ inline int kth_bin(const uint32_t* hist, int k, int lane) {
+  uint32_t r = 0;
+  for (int j = 0; j < 64; ++j) r += hist[64 * lane + ((j + lane) & 63)];
+  uint32_t suf = r;  // count of rows lane .. 63
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(suf, off);
+    if (lane + off < 64) suf += y;
+  }
+  const uint64_t rows = __ballot(suf >= (uint32_t)k);
+  if (rows == 0) return 0;
+  const int row = 63 - __builtin_clzll(rows);
+  const uint32_t above = __shfl(suf, row) - __shfl(r, row);  // count of the rows above it
+  uint32_t t = hist[64 * row + lane];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(t, off);
+    if (lane + off < 64) t += y;
+  }
+  const uint64_t bins = __ballot(above + t >= (uint32_t)k);
+  return 64 * row + (63 - __builtin_clzll(bins));
+}
 
 template <typename Kv>
 __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(ScoreArgs a, WorkList wl) {
@@ -94,7 +123,14 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
       l2[mb][j] = a.lse2[(size_t)i * kHeads + 32 * mb + 8 * (j >> 2) + hrow + (j & 3)];
   __syncthreads();  // histogram cleared; the loads above have completed
 
-  float* srow = a.scores + (size_t)i * a.score_stride;
+  // This wave's list of candidates: (score bits, position) of every score whose first
+  // digit is at least the running threshold `thr` when its tile is flushed. thr is the
+  // bin of the k-th largest score the workgroup has seen so far (kth_bin of its
+  // histogram): a key below it has k keys of this split ahead of it and cannot be among
+  // the query's top k.
+  const size_t wl_idx = ((size_t)i * a.n_split + split) * kSWaves + wave;
+  uint2* mylist = a.lists + wl_idx * a.list_cap;
+  int thr = 0, cnt = 0;
   const int ntw = wave < ntiles ? (ntiles - wave + kSWaves - 1) / kSWaves : 0;
   // Tiles in the reverse of the attention pass's rotated order (same rotation): the first
   // tiles read here are the last that pass read, some still in the last-level cache.
@@ -137,28 +173,36 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
       atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
     }
     if ((it + 1) % kSFlush == 0 || it + 1 == ntw) {
-      // write the staged tiles in a burst: lane e stores 4 scores of tile first + e/8
-      // (16 bytes), so the writes interleave with the streaming reads as little as possible
-      wait_lgkm0();
+      // flush the staged tiles: the scores that pass the running threshold, compacted
+      // with a ballot into the wave's list (a burst of 8-byte writes)
+      wait_lgkm0();  // this wave's staged scores and histogram counts are in LDS
+      thr = max(thr, kth_bin(sm.hist, a.top_k, lane));
       const int first = (it / kSFlush) * kSFlush;
-      const int nt = it + 1 - first;
-      for (int e = lane; e < nt * 8; e += 64) {
-        const int tt = first + e / 8;
-        const int q0 = k0 + tile_of(wave + tt * kSWaves) * kTile + (e % 8) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(&sm.sbuf[wave][(tt - first) * kTile + (e % 8) * 4]);
-        if (q0 + 3 < k1) {
-          *reinterpret_cast<float4*>(srow + q0) = v;
-        } else {
-          if (q0 < k1) srow[q0] = v.x;
-          if (q0 + 1 < k1) srow[q0 + 1] = v.y;
-          if (q0 + 2 < k1) srow[q0 + 2] = v.z;
+      const int ne = (it + 1 - first) * kTile;
+      for (int e0 = 0; e0 < ne; e0 += 64) {
+        const int e = e0 + lane;
+        const int p = k0 + tile_of(wave + (first + e / kTile) * kSWaves) * kTile + (e % kTile);
+        const uint32_t u = e < ne ? __float_as_uint(sm.sbuf[wave][e]) : 0u;
+        const bool keep = e < ne && p < k1 && (int)(u >> kHistShift) >= thr;
+        const uint64_t bal = __ballot(keep);
+        if (keep) {
+          const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          mylist[cnt + below] = make_uint2(u, (uint32_t)p);
         }
+        cnt += __popcll(bal);
       }
     }
   }
+  if (lane == 0) a.list_count[wl_idx] = cnt;
   __syncthreads();
+  // the split's final threshold (every score of the split is in the histogram now; each
+  // wave finds the same): only the scores at or above it are kept, and only those are
+  // counted in the query's histogram
+  const int thr_final = kth_bin(sm.hist, a.top_k, lane);
+  if (threadIdx.x == 0) a.list_thr[(size_t)i * a.n_split + split] = thr_final;
   uint32_t* hq = a.hist + (size_t)i * kHistBins;
-  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) {
+  for (int e = thr_final + threadIdx.x; e < kHistBins; e += blockDim.x) {
     const uint32_t c = sm.hist[e];
     if (c) atomicAdd(&hq[e], c);
   }

@@ -11,11 +11,14 @@
 // order like the values; the 64-bit key ((bits << 32) | ~position) is then unique per
 // candidate and its k largest values are exactly the selection.
 //
-// Two kernels (the score pass already built a histogram of bits 30..19 of every
-// candidate's score):
+// Two kernels (the score pass already built a histogram of bits 30..19 of the scores it
+// kept, and kept either every candidate's score in a row or, in the decode-shaped
+// selector, per-split lists of the (score, position) pairs that can still be among the
+// top k):
 //   filter  (many workgroups per query): from the histogram, find the bin b1 that holds
-//           the k-th largest; keys of a chunk in a larger bin are selected outright, keys
-//           in b1 are copied to a per-query candidate list (up to kCandCap).
+//           the k-th largest; keys of a chunk (or of a split's lists) in a larger bin are
+//           selected outright, keys in b1 are copied to a per-query candidate list (up to
+//           kCandCap).
 //   finish  (one workgroup per query): radix-select the remaining r keys among the b1
 //           candidates in LDS (or, if b1 overflowed the list, by streaming the query's
 //           scores again), then order the k positions ascending and write them.
@@ -179,6 +182,62 @@ __device__ void filter_chunk(const TopkArgs& a, int i, int nc, int split, uint32
   }
 }
 
+// Filter over the candidate lists of score split `split` of query i (the lists of the
+// split's waves, concatenated): entries above the threshold bin b1 go to `above`, those in
+// it to `cand`. Thread t takes entries t, t + 256, ...: a first sweep counts them, one
+// atomic per list reserves the workgroup's slots, a second sweep (the entries again, now
+// from the L2) writes each thread's run.
+__device__ void filter_lists(const TopkArgs& a, int i, int nc, int split, uint32_t* s_wave, int* s_res,
+                             uint32_t* s_tot) {
+  if (split * a.list_split_keys >= nc) return;  // the score pass has no list for it
+  int b1, above;
+  threshold_bin(a.hist + (size_t)i * kHistBins, a.top_k, s_wave, s_res, b1, above);
+  const size_t l0 = ((size_t)i * a.list_splits + split) * a.list_waves;
+  int off[9];  // start of each list in the concatenation (lists past list_waves are empty)
+  off[0] = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) off[w + 1] = off[w] + (w < a.list_waves ? a.list_count[l0 + w] : 0);
+  const int total = off[8];
+  auto entry = [&](int e) {
+    int w = 0, j = e;
+#pragma unroll
+    for (int q = 1; q < 8; ++q)
+      if (e >= off[q]) {
+        w = q;
+        j = e - off[q];
+      }
+    return a.lists[(l0 + w) * a.list_cap + j];
+  };
+  uint32_t na = 0, nb = 0;
+  for (int e = threadIdx.x; e < total; e += kThreads) {
+    const int d = (int)(entry(e).x >> kHistShift);
+    na += d > b1 ? 1u : 0u;
+    nb += d == b1 ? 1u : 0u;
+  }
+  uint32_t ta, tb;
+  const uint32_t pa = block_excl_scan(na, s_wave, ta);
+  const uint32_t pb = block_excl_scan(nb, s_wave, tb);
+  if (threadIdx.x == 0) {
+    s_tot[0] = ta ? atomicAdd(&a.counters[(size_t)i * 4 + 0], ta) : 0u;
+    s_tot[1] = tb ? atomicAdd(&a.counters[(size_t)i * 4 + 1], tb) : 0u;
+  }
+  __syncthreads();
+  uint32_t oa = s_tot[0] + pa, ob = s_tot[1] + pb;
+  int32_t* abv = a.above + (size_t)i * a.top_k;
+  uint2* cand = a.cand + (size_t)i * kCandCap;
+  for (int e = threadIdx.x; e < total; e += kThreads) {
+    const uint2 c = entry(e);
+    const int d = (int)(c.x >> kHistShift);
+    if (d > b1) {
+      if (oa < (uint32_t)a.top_k) abv[oa] = (int32_t)c.y;
+      ++oa;
+    } else if (d == b1) {
+      if (ob < (uint32_t)kCandCap) cand[ob] = c;
+      ++ob;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // Selection inside the threshold bin. The r largest elements by (score bits, then
 // smaller position) are found by a radix select over the 19 score bits below the first
@@ -209,16 +268,38 @@ struct SelShared {
   };
 };
 
+// Where the scores of query i are: a score row of nc entries (sc), or the candidate lists
+// of the score pass (a->lists set).
+struct ElemSource {
+  const float* sc;
+  int nc;
+  const TopkArgs* a;
+  int i;
+};
+
 // Visits the threshold-bin elements: from LDS (n elements) or by streaming the scores.
 template <bool kLds, typename F>
-__device__ inline void for_each_elem(const SelShared& sh, uint32_t n, const float* __restrict__ sc,
-                                     int nc, int b1, F&& f) {
+__device__ inline void for_each_elem(const SelShared& sh, uint32_t n, const ElemSource& src, int b1, F&& f) {
   if (kLds) {
     for (uint32_t e = threadIdx.x; e < n; e += kThreads) f(sh.cu[e], sh.cp[e]);
-  } else {
-    for (int p = threadIdx.x; p < nc; p += kThreads) {
-      const uint32_t u = __float_as_uint(sc[p]);
+  } else if (src.a->lists == nullptr) {
+    for (int p = threadIdx.x; p < src.nc; p += kThreads) {
+      const uint32_t u = __float_as_uint(src.sc[p]);
       if ((int)(u >> kHistShift) == b1) f(u & kLowMask, (uint32_t)p);
+    }
+  } else {
+    // every kept list entry of the query: entries of bin b1 are at or above each split's
+    // threshold (b1 is the query's k-th, at least each split's k-th)
+    const TopkArgs& a = *src.a;
+    const int ns = min(a.list_splits, (src.nc + a.list_split_keys - 1) / a.list_split_keys);
+    for (int l = 0; l < ns * a.list_waves; ++l) {
+      const size_t li = (size_t)src.i * a.list_splits * a.list_waves + l;
+      const int n_l = a.list_count[li];
+      const uint2* lst = a.lists + li * a.list_cap;
+      for (int e = threadIdx.x; e < n_l; e += kThreads) {
+        const uint2 c = lst[e];
+        if ((int)(c.x >> kHistShift) == b1) f(c.x & kLowMask, c.y);
+      }
     }
   }
 }
@@ -227,14 +308,14 @@ __device__ inline void for_each_elem(const SelShared& sh, uint32_t n, const floa
 // whose key matches `prefix` above the digit, then the digit value holding the r-th
 // largest and the count of larger elements. key(ul, p) is given by `key_of`.
 template <bool kLds, typename K>
-__device__ inline void digit_pass(SelShared& sh, uint32_t n, const float* __restrict__ sc, int nc, int b1,
+__device__ inline void digit_pass(SelShared& sh, uint32_t n, const ElemSource& src, int b1,
                                   K&& key_of, uint64_t prefix, int shift, int width, int r, int& digit,
                                   int& larger) {
   const int nbins = 1 << width;
   for (int e = threadIdx.x; e < nbins; e += kThreads) sh.hist[e] = 0u;
   __syncthreads();
   const int hi = shift + width;
-  for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t p) {
+  for_each_elem<kLds>(sh, n, src, b1, [&](uint32_t ul, uint32_t p) {
     const uint64_t key = key_of(ul, p);
     if ((key >> hi) == (prefix >> hi)) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & (uint32_t)(nbins - 1)], 1u);
   });
@@ -271,22 +352,22 @@ __device__ inline void digit_pass(SelShared& sh, uint32_t n, const float* __rest
 }
 
 template <bool kLds>
-__device__ void select_in_bin(SelShared& sh, uint32_t n, const float* __restrict__ sc, int nc, int b1,
+__device__ void select_in_bin(SelShared& sh, uint32_t n, const ElemSource& src, int b1,
                               int r_need) {
   auto score_key = [](uint32_t ul, uint32_t) { return (uint64_t)ul; };
   uint64_t pre = 0;
   int r = r_need, dg, lg;
-  digit_pass<kLds>(sh, n, sc, nc, b1, score_key, pre, 8, 11, r, dg, lg);
+  digit_pass<kLds>(sh, n, src, b1, score_key, pre, 8, 11, r, dg, lg);
   pre |= (uint64_t)dg << 8;
   r -= lg;
-  digit_pass<kLds>(sh, n, sc, nc, b1, score_key, pre, 0, 8, r, dg, lg);
+  digit_pass<kLds>(sh, n, src, b1, score_key, pre, 0, 8, r, dg, lg);
   pre |= (uint64_t)dg;
   r -= lg;
   const uint32_t ustar = (uint32_t)pre;  // score bits of the r_need-th largest
   // r elements with score bits == ustar are still needed; ties go to smaller positions
   if (threadIdx.x == 0) sh.res[2] = 0;
   __syncthreads();
-  for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t) {
+  for_each_elem<kLds>(sh, n, src, b1, [&](uint32_t ul, uint32_t) {
     if (ul == ustar) atomicAdd(&sh.res[2], 1);
   });
   __syncthreads();
@@ -299,14 +380,14 @@ __device__ void select_in_bin(SelShared& sh, uint32_t n, const float* __restrict
     uint64_t tp = (uint64_t)1 << 32;
     int rr = r;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      digit_pass<kLds>(sh, n, sc, nc, b1, tie_key, tp, shift, 8, rr, dg, lg);
+      digit_pass<kLds>(sh, n, src, b1, tie_key, tp, shift, 8, rr, dg, lg);
       tp |= (uint64_t)dg << shift;
       rr -= lg;
     }
     pstar_inv = (uint32_t)tp;
   }
   __syncthreads();
-  for_each_elem<kLds>(sh, n, sc, nc, b1, [&](uint32_t ul, uint32_t p) {
+  for_each_elem<kLds>(sh, n, src, b1, [&](uint32_t ul, uint32_t p) {
     const bool take = ul > ustar || (ul == ustar && (~p) >= pstar_inv);
     if (take) {
       const uint32_t slot = atomicAdd(&sh.nsel, 1u);
@@ -328,7 +409,7 @@ __device__ void finish_query(const TopkArgs& a, SelShared& sh, int i, int nc, in
   const int32_t* abv = a.above + (size_t)i * k;
   for (int e = threadIdx.x; e < above; e += kThreads) sh.sel[e] = __builtin_nontemporal_load(&abv[e]);
   if (threadIdx.x == 0) sh.nsel = (uint32_t)above;
-  const float* sc = a.scores + (size_t)i * a.score_stride;
+  const ElemSource src{a.scores ? a.scores + (size_t)i * a.score_stride : nullptr, nc, &a, i};
   if (n_bin <= (uint32_t)kCandCap) {
     const uint2* cand = a.cand + (size_t)i * kCandCap;
     for (uint32_t e = threadIdx.x; e < n_bin; e += kThreads) {
@@ -338,10 +419,10 @@ __device__ void finish_query(const TopkArgs& a, SelShared& sh, int i, int nc, in
       sh.cp[e] = cy;
     }
     __syncthreads();
-    select_in_bin<true>(sh, n_bin, sc, nc, b1, r_need);
+    select_in_bin<true>(sh, n_bin, src, b1, r_need);
   } else {
     __syncthreads();
-    select_in_bin<false>(sh, 0, sc, nc, b1, r_need);
+    select_in_bin<false>(sh, 0, src, b1, r_need);
   }
   // ascending order: bucket by position (kBuckets equal ranges of [0, nc)), prefix sums,
   // scatter, then the rank inside a bucket (buckets hold ~1 position on average)
@@ -404,6 +485,20 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
   filter_chunk(a, i, nc, split, s_wave, s_res, s_tot);
 }
 
+__global__ __launch_bounds__(kThreads) void topk_filter_lists_kernel(TopkArgs a) {
+  __shared__ uint32_t s_wave[kThreads / 64];
+  __shared__ int s_res[4];
+  __shared__ uint32_t s_tot[2];
+  const int i = blockIdx.x / a.list_splits;
+  const int split = blockIdx.x - i * a.list_splits;
+  int64_t base;
+  int t;
+  if (!query_desc(a.b, i, base, t) || plan_missed(a, i)) return;
+  const int nc = cand_count(t, a.window);
+  if (a.top_k == 0 || nc <= a.top_k) return;
+  filter_lists(a, i, nc, split, s_wave, s_res, s_tot);
+}
+
 __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
   __shared__ SelShared sh;
   const int i = blockIdx.x;
@@ -439,7 +534,10 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
 }  // namespace
 
 hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(topk_filter_kernel, dim3(a.b.total_q * a.n_split), dim3(kThreads), 0, s, a);
+  if (a.lists)
+    hipLaunchKernelGGL(topk_filter_lists_kernel, dim3(a.b.total_q * a.list_splits), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(a.b.total_q * a.n_split), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

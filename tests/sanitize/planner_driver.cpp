@@ -143,6 +143,12 @@ static void score_common(const ScoreArgs& a, const WorkList& wl) {
   in_ws(a.lse2, (size_t)a.b.total_q * kHeads * 4);
   in_ws(a.plan_miss, (size_t)a.b.total_q * 4);
   CHECK((int64_t)a.n_split * a.split_keys >= (int64_t)a.b.max_kv_len - a.window + 1 || wl.n > 0);
+  CHECK((a.scores == nullptr) != (a.lists == nullptr));
+  if (a.lists) {  // the regions of all of a split's lists are checked by the top-k stubs
+    CHECK(a.list_cap >= 32 && a.list_cap % 32 == 0);
+    CHECK((int64_t)a.list_cap * 8 >= a.split_keys);
+    in_ws(a.list_thr, (size_t)a.b.total_q * a.n_split * sizeof(int32_t));
+  }
 }
 hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t) {
   score_common(a, WorkList{});
@@ -174,6 +180,15 @@ static void topk_common(const TopkArgs& a) {
   in_ws(a.counters, (size_t)a.b.total_q * 16);
   in_ws(a.miss_attn, (size_t)a.b.total_q * 4);
   in_ws(a.miss_score, (size_t)a.b.total_q * 4);
+  if (a.lists) {
+    CHECK(a.scores == nullptr && (a.list_waves == 4 || a.list_waves == 8));
+    CHECK((int64_t)a.list_splits * a.list_split_keys >= (int64_t)a.b.max_kv_len - a.window + 1);
+    CHECK((int64_t)a.list_cap * a.list_waves >= a.list_split_keys);
+    const size_t nl = (size_t)a.b.total_q * a.list_splits * a.list_waves;
+    in_ws(a.lists, nl * a.list_cap * sizeof(uint2));
+    in_ws(a.list_count, nl * sizeof(int32_t));
+    in_ws(a.list_thr, (size_t)a.b.total_q * a.list_splits * sizeof(int32_t));
+  }
 }
 hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t) {
   topk_common(a);
