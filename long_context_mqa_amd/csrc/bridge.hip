@@ -21,6 +21,14 @@
 // 32-deep stages, which measured 15% slower on random data even with a third stage).
 // Tiles of the same rows run back to back on one XCD, so H is read from HBM once and
 // re-served from that XCD's L2 for the other column tiles.
+//
+// The results leave through LDS: a store straight from the MFMA layout writes 32 rows x 16
+// bytes per instruction, and those stores cost about 10% of the kernel; written as bf16 rows
+// into the (then idle) stage area and read back, each store instruction covers four whole
+// 256-byte rows (5% faster overall). Measured and not kept: four waves (one per SIMD) on
+// 256 x 256 tiles with AGPR accumulators and double-buffered operand registers (2% slower);
+// a persistent grid carrying the copy stream across tiles (8% slower); touching the lines of
+// stage k+3 ahead of their copies (4% slower: the copies were not waiting on HBM).
 #include "kernel_common.h"
 #include "hs2_launch.h"
 
@@ -84,8 +92,9 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
   constexpr int kCopB = kBM / kRowsPerCopy / kGWaves;
   static_assert(kCopA * kRowsPerCopy * kGWaves == kCols && kCopB * kRowsPerCopy * kGWaves == kBM,
                 "copies must split evenly");
-  __shared__ __align__(16) uint8_t lds_a[kStagesG][kTA];
-  __shared__ __align__(16) uint8_t lds_b[kStagesG][kTB];
+  __shared__ __align__(16) uint8_t lds_all[kStagesG * (kTA + kTB)];
+  uint8_t(*lds_a)[kTA] = reinterpret_cast<uint8_t(*)[kTA]>(lds_all);
+  uint8_t(*lds_b)[kTB] = reinterpret_cast<uint8_t(*)[kTB]>(lds_all + kStagesG * kTA);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_nt = a.n_mats * kDim / kCols;
@@ -166,26 +175,47 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
     }
   }
 
-  // C^T[n][row]: lane holds rows 32*y + l%32, columns 32*x + 8*(j/4) + 4*(l/32) + j%4
+  // Results through LDS, 128 rows at a time: the waves holding those rows write them as bf16
+  // rows of kCols columns, then every store instruction writes four whole 256-byte rows of one
+  // output matrix. C^T[n][row]: lane l holds rows 32 y + l % 32, columns 32 x + 8 jg + 4 (l / 32)
+  // + 0..3 of block (x, y).
+  constexpr int kPitch = kCols * 2 + 16;
+  static_assert(128 * kPitch <= kStagesG * (kTA + kTB), "a half tile fits in the stage area");
+  uint8_t* epi = lds_all;  // the stage area, free once every wave is past the last stage
+  const int last = (int)(a.n_rows - r0 < kBM ? a.n_rows - r0 : kBM) - 1;
+  constexpr int kSegs = 128 / 4 * (kCols / kDim);  // 1 KB stores per half tile
 #pragma unroll
-  for (int y = 0; y < kYB; ++y) {
-    const int64_t grow = r0 + wr * kWR + 32 * y + (lane & 31);
-    if (grow >= a.n_rows) continue;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // stage reads (or the previous half's stores) are done
+    if ((wr * kWR) / 128 == half) {
 #pragma unroll
-    for (int x = 0; x < kXB; ++x) {
-      const int gc = nt * kCols + wc * kWC + 32 * x;  // first output column of the block
-      uint16_t* out = a.outs[gc / kDim];
+      for (int y = 0; y < kYB; ++y)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int n0 = gc % kDim + 8 * jg + 4 * (lane >> 5);
-        __bf16 v4[4];
+        for (int x = 0; x < kXB; ++x)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v4[q] = (__bf16)acc[x][y][4 * jg + q];
-        *reinterpret_cast<uint2*>(out + grow * kDim + n0) = __builtin_bit_cast(uint2, v4);
-      }
+          for (int jg = 0; jg < 4; ++jg) {
+            __bf16 v4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v4[q] = (__bf16)acc[x][y][4 * jg + q];
+            const int row = wr * kWR - 128 * half + 32 * y + (lane & 31);
+            const int col = wc * kWC + 32 * x + 8 * jg + 4 * (lane >> 5);
+            *reinterpret_cast<uint2*>(epi + row * kPitch + col * 2) = __builtin_bit_cast(uint2, v4);
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSegs / kGWaves; ++i) {
+      const int idx = wave * (kSegs / kGWaves) + i;
+      const int m = idx / 32;                        // output matrix of the tile
+      const int row = (idx % 32) * 4 + (lane >> 4);  // row within the half
+      const uint4 v = *reinterpret_cast<const uint4*>(epi + row * kPitch + m * 256 + (lane & 15) * 16);
+      const int trow = 128 * half + row;
+      if (trow <= last)
+        *reinterpret_cast<uint4*>(a.outs[nt * (kCols / kDim) + m] + (r0 + trow) * kDim + (lane & 15) * 8) = v;
     }
   }
 }
+
 
 }  // namespace
 
