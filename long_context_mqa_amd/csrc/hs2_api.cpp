@@ -223,12 +223,15 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt, b
 
 struct SparsePlan {
   Split attn;
+  bool narrow = false;  // bf16 / FP8: the narrow-slot kernel, one workgroup per query
   size_t total = 0;
 };
 
 // bf16 and FP8 K/V: slices of whole tiles, at most sparse_slots() of them in LDS at once,
-// sized so that the launch holds about one workgroup per CU; fp32 K/V: key splits of the
-// fp32 gather kernel (at most kSparseSplitMax keys, the bound of its LDS row list).
+// sized so that the launch holds about one workgroup per CU; a batch of at least two
+// queries per CU instead takes the narrow-slot kernel with one workgroup per query (two
+// workgroups share a CU; no split combine). fp32 K/V: key splits of the fp32 gather kernel
+// (at most kSparseSplitMax keys, the bound of its LDS row list).
 SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
   SparsePlan p;
   const int64_t tq = std::max(0, b->total_q);
@@ -239,6 +242,10 @@ SparsePlan plan_sparse(const hs2_seqs* b, int window, int top_k, hs2_dtype dt) {
       p.attn.split_keys = kSparseSplitMax;
       p.attn.n_split = (int)ceil_div(max_keys, kSparseSplitMax);
     }
+  } else if (tq >= 2 * kTargetGroups) {
+    p.narrow = true;
+    p.attn.split_keys = (int)(std::max<int64_t>(1, ceil_div(max_keys, kTile)) * kTile);
+    p.attn.n_split = 1;
   } else {
     const int64_t tiles = std::max<int64_t>(1, ceil_div(max_keys, kTile));
     int64_t per = std::min<int64_t>(ceil_div(std::max<int64_t>(1, tq) * tiles, kTargetGroups),
@@ -594,7 +601,7 @@ hs2_status sparse_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   LaunchMarks mk(s);
   hipError_t e = mk.before(0);
   if (e == hipSuccess)
-    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s) : launch_sparse_attn(a, fp8, grid, s);
+    e = f32 ? launch_attn_f32(a, true, grid, nullptr, nullptr, s) : launch_sparse_attn(a, fp8, p.narrow, grid, s);
   if (e == hipSuccess) e = mk.after(0);
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   if (p.attn.n_split > 1) {

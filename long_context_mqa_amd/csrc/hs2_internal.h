@@ -23,6 +23,7 @@ constexpr int kCandCap = 4096; // threshold-bin candidates kept per query for th
 constexpr int kQTile = 8;      // queries per q-tile of the chunked selector (one wave each)
 constexpr int kScoreSplitMax = 32768;  // keys per chunked score workgroup (16-bit LDS bin counts)
 constexpr int kSparseStageBytes = 147456;  // LDS of a sparse-layer workgroup's K/V tile slots
+constexpr int kSparseNarrowBytes = 65536;  // ... in the narrow form (batches of many queries)
 // K/V tiles (32 rows each) a sparse-layer workgroup holds in LDS at once
 constexpr int sparse_slots(bool fp8) { return kSparseStageBytes / (2 * kTile * kDim * (fp8 ? 1 : 2)); }
 constexpr float kLog2e = 1.4426950408889634f;

@@ -26,7 +26,7 @@ hipError_t launch_attn_fp8kv(const AttnArgs& a, const WorkList& wl, int grid, ui
 hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* hist,
                            uint32_t* counters, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, bool f32, hipStream_t s);
-hipError_t launch_sparse_attn(const AttnArgs& a, bool fp8, int grid, hipStream_t s);
+hipError_t launch_sparse_attn(const AttnArgs& a, bool fp8, bool narrow, int grid, hipStream_t s);
 hipError_t launch_qtile_prep(const SeqsDev& b, int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_attn_chunk(const AttnArgs& a, const int2* tiles, int max_tiles, hipStream_t s);
 hipError_t launch_score_chunk(const ScoreArgs& a, const int2* tiles, int max_tiles, hipStream_t s);

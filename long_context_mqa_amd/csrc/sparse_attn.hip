@@ -31,9 +31,14 @@ using namespace attn;
 
 constexpr int kSpWaves = 4;                 // waves per workgroup: 2 head blocks x 2 tile parities
 
+// Tile slots of a workgroup: the wide form (144 KB of LDS, one workgroup per CU) for
+// batches whose slices fill the GPU about once; the narrow form (64 KB, two per CU, so
+// one's gather overlaps the other's arithmetic) for batches of many queries, where each
+// workgroup takes a whole query in batches of kNarrow tiles.
 template <typename Kv>
 struct SparseCfg {
   static constexpr int kSlots = kSparseStageBytes / (2 * Kv::kTileBytes);  // 9 bf16 tiles, 18 FP8 tiles
+  static constexpr int kNarrow = kSparseNarrowBytes / (2 * Kv::kTileBytes);  // 4 bf16 tiles, 8 FP8 tiles
 };
 static_assert(SparseCfg<KvBf16>::kSlots == sparse_slots(false) && SparseCfg<KvFp8>::kSlots == sparse_slots(true),
               "slots");
@@ -192,12 +197,11 @@ struct SparseKeys {
 // copying its K rows and the one of head block 1 its V rows. Each round of two tiles ends
 // with a barrier of the workgroup, after each wave has waited for its own copies. The
 // first batch's slot values come in `slot0` (this wave's tiles j = 2u + par).
-template <typename Kv, bool kMaxOnly>
+template <typename Kv, int T, bool kMaxOnly>
 __device__ inline void sparse_pass(HeadsState& st, float& mx, uint8_t (*stage)[2][Kv::kTileBytes],
-                                   const SparseKeys& sk, const int32_t (&slot0)[(SparseCfg<Kv>::kSlots + 1) / 2],
-                                   int ntiles, const bf16x8 (&q)[8], const void* __restrict__ kp,
-                                   const void* __restrict__ vp, float c2, int hb, int par, int lane) {
-  constexpr int T = SparseCfg<Kv>::kSlots;
+                                   const SparseKeys& sk, const int32_t (&slot0)[(T + 1) / 2], int ntiles,
+                                   const bf16x8 (&q)[8], const void* __restrict__ kp, const void* __restrict__ vp,
+                                   float c2, int hb, int par, int lane) {
   constexpr int U = (T + 1) / 2;  // tiles of one parity in a batch
   uint32_t vb[4];
   vt_bases_of<Kv>(lane, vb);
@@ -251,17 +255,18 @@ __device__ inline void sparse_pass(HeadsState& st, float& mx, uint8_t (*stage)[2
   }
 }
 
-template <typename Kv>
+template <typename Kv, int T>
 __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) {
-  constexpr int T = SparseCfg<Kv>::kSlots;
   constexpr int U = (T + 1) / 2;
   // K/V slots during the key loop; afterwards the state of the parity-1 waves for the merge
   struct MergeArea {
     float o[2][64 * 64];  // [head block][register image: element e of lane l at e * 64 + l]
     float m[2][32], l[2][32], le[2][32];
   };
-  static_assert(sizeof(MergeArea) <= T * 2 * Kv::kTileBytes, "merge area");
-  __shared__ __align__(16) uint8_t stage[T][2][Kv::kTileBytes];
+  constexpr int kSlotBytes = T * 2 * Kv::kTileBytes;
+  constexpr int kBytes = kSlotBytes > (int)sizeof(MergeArea) ? kSlotBytes : (int)sizeof(MergeArea);
+  __shared__ __align__(16) uint8_t lds[kBytes];
+  uint8_t(*stage)[2][Kv::kTileBytes] = reinterpret_cast<uint8_t(*)[2][Kv::kTileBytes]>(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hb = wave & 1, par = wave >> 1;
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) 
   HeadsState st;
   heads_init(st);
   float mx = -INFINITY;
-  sparse_pass<Kv, false>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
+  sparse_pass<Kv, T, false>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
   // rare: a logit far above the first tile's maximum overflowed a wave's sums. Every wave
   // then gathers the slice again (each copies its share of the tiles and joins every
   // barrier): once for the exact maximum of each head over its tiles, once more with it
@@ -327,12 +332,12 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) 
   if (lane == 0) s_bad[wave] = finite ? 0 : 1;
   __syncthreads();  // also: every wave is done with the slots
   if (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) {
-    sparse_pass<Kv, true>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
+    sparse_pass<Kv, T, true>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
     heads_init(st);
     st.m = mx;
     st.have_ref = 1;
     slot_barrier();
-    sparse_pass<Kv, false>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
+    sparse_pass<Kv, T, false>(st, mx, stage, sk, slot0, ntiles, q, a.k, a.v, a.c2, hb, par, lane);
     __syncthreads();  // the slots are free for the merge area
   }
   st.l += __shfl_xor(st.l, 32);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) 
 
   // merge the two parities of each head block (fixed order: parity 0, then 1); a wave that
   // attended no key (a slice of a single tile) has the "no key yet" reference and weight 0
-  MergeArea& mg = *reinterpret_cast<MergeArea*>(&stage[0][0][0]);
+  MergeArea& mg = *reinterpret_cast<MergeArea*>(lds);
   if (par == 1) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -398,11 +403,15 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) 
 
 }  // namespace
 
-hipError_t launch_sparse_attn(const AttnArgs& a, bool fp8, int grid, hipStream_t s) {
-  if (fp8)
-    hipLaunchKernelGGL(sparse_attn_kernel<KvFp8>, dim3(grid), dim3(64 * kSpWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL(sparse_attn_kernel<KvBf16>, dim3(grid), dim3(64 * kSpWaves), 0, s, a);
+hipError_t launch_sparse_attn(const AttnArgs& a, bool fp8, bool narrow, int grid, hipStream_t s) {
+  const dim3 g(grid), blk(64 * kSpWaves);
+  if (fp8) {
+    if (narrow) hipLaunchKernelGGL((sparse_attn_kernel<KvFp8, SparseCfg<KvFp8>::kNarrow>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_kernel<KvFp8, SparseCfg<KvFp8>::kSlots>), g, blk, 0, s, a);
+  } else {
+    if (narrow) hipLaunchKernelGGL((sparse_attn_kernel<KvBf16, SparseCfg<KvBf16>::kNarrow>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_kernel<KvBf16, SparseCfg<KvBf16>::kSlots>), g, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -99,7 +99,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, bool gather, int grid, uint32_t* h
   attn_common(a, WorkList{}, gather, grid, hist, counters);
   return hipSuccess;
 }
-hipError_t launch_sparse_attn(const AttnArgs& a, bool, int grid, hipStream_t) {
+hipError_t launch_sparse_attn(const AttnArgs& a, bool, bool, int grid, hipStream_t) {
   ++g_launches;
   CHECK(grid == a.b.total_q * a.n_split && a.split_keys % kTile == 0 && a.split_keys >= kTile);
   CHECK(a.n_split <= 256 || a.split_keys > sparse_slots(false) * kTile);

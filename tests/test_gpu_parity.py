@@ -150,6 +150,30 @@ def test_chunked_ragged_queries():
     check_all_queries_properties(inp, g)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_sparse_layer_many_queries(dtype):
+    """A batch of at least two queries per CU (620 here) takes the sparse layer's narrow-slot
+    form, one workgroup per query: every query's sparse output against the oracle on the
+    GPU's own selection, with t < window, at most k candidates and long slices all present;
+    the selector on a sample of them."""
+    rng = np.random.default_rng(31)
+    seqs = [1500, 5000, 300]
+    qpos = [sorted(set([0, 5, 127, 128, 600, 1151, 1152, 1499] + rng.integers(0, 1500, 200).tolist())),
+            sorted(set([127, 1200, 4999] + rng.integers(1000, 5000, 300).tolist())),
+            sorted(set([0, 1, 200, 299] + rng.integers(0, 300, 130).tolist()))]
+    spec = BlockSpec("many-queries", seqs, qpos, dtype=dtype, n_sparse=1, needles_per_query=1, seed=33)
+    assert spec.total_q >= 512
+    inp = make_block_inputs(spec)
+    _say(f"sparse many queries {dtype}: {spec.total_q} queries")
+    g = run_block(inp)
+    check_all_queries_properties(inp, g)
+    rr = dtype == "fp8"
+    for qi in range(spec.total_q):
+        ref, _ = oracle_sparse(inp, qi, 0, g["sel"][qi])
+        check_attn(g["sparse"][0][qi], ref, f"many-queries q{qi} sparse", beyond_rounding=rr)
+    check_queries(inp, g, range(0, spec.total_q, 26), f"many-queries-{dtype}")
+
+
 def test_small_context_sparse_equals_full_on_gpu():
     """When t+1 <= window + top_k, the sparse layer with the selector's own Q reproduces
     the selector's output (the <= 1,152-row invariant)."""
@@ -631,14 +655,15 @@ def test_workload5_bridge_and_ragged_decode():
     _full(5, range(32))
 
 
-@pytest.mark.parametrize("shape", ["decode", "chunk", "decode-fp8"])
+@pytest.mark.parametrize("shape", ["decode", "chunk", "decode-fp8", "many"])
 def test_logit_far_above_first_tile_is_recomputed(shape):
     """Keys whose logits for one head lie 150..402 (log2 units) above the other keys, at
     increasing positions over ~16 tiles: a wave whose first tile holds none of them (or
     a smaller one) overflows sums taken against that tile's maximum, and must detect it
     and recompute with its exact maximum. Covers the decode-shaped selector kernel, the
     q-tile selector kernel and the sparse kernel (whose Q equals the selector's, with
-    enough queries that its waves take two tiles each)."""
+    enough queries that its waves take two tiles each; with 520 queries, the narrow-slot
+    form, whose workgroup takes the query's 36 tiles in batches)."""
     if shape == "decode":
         spec = BlockSpec("spike-decode", [2000] * 40, [[1999]] * 40, dtype="bf16", n_sparse=1,
                          needles_per_query=0, seed=21)
@@ -646,9 +671,12 @@ def test_logit_far_above_first_tile_is_recomputed(shape):
         # FP8 keys: a K scale large enough for the spike keys (components up to ~90)
         spec = BlockSpec("spike-decode-fp8", [2000] * 40, [[1999]] * 40, dtype="fp8", n_sparse=1,
                          needles_per_query=0, seed=23, k_scale=0.25)
-    else:
+    elif shape == "chunk":
         spec = BlockSpec("spike-chunk", [5000], [list(range(4990, 5000))], dtype="bf16", n_sparse=1,
                          needles_per_query=0, seed=22)
+    else:
+        spec = BlockSpec("spike-many", [5000], [list(range(4480, 5000))], dtype="bf16", n_sparse=1,
+                         needles_per_query=0, seed=24)
     inp = make_block_inputs(spec)
     qi, h = 0, 5
     base = int(inp.kv_start[int(inp.q_seq[qi])])
@@ -668,7 +696,7 @@ def test_logit_far_above_first_tile_is_recomputed(shape):
         assert np.all(np.diff(xs) > 0)
     _say(f"spike {shape}: x in [{xs.min():.1f}, {xs.max():.1f}]")
     g = run_block(inp)
-    check_queries(inp, g, range(spec.total_q), f"spike-{shape}")
+    check_queries(inp, g, range(spec.total_q) if spec.total_q < 64 else [0, 1, 7, 259, 519], f"spike-{shape}")
     assert int(pos[int(np.argmax(xs))]) in set(g["sel"][qi].tolist())
 
 
