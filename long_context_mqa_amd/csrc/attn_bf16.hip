@@ -73,11 +73,30 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int e = tid; e < per; e += blockDim.x) a.hist[(size_t)i * kHistBins + slab * per + e] = 0u;
     if (slab == 0 && tid < 4) a.counters[(size_t)i * 4 + tid] = 0u;
   }
+  // The partials are loaded kMergeBatch at a time, every load of a batch in flight at once,
+  // and merged in split order; the first batch goes out with the query's descriptor loads
+  // (partials past the query's valid splits are in the workspace and simply not used).
+  constexpr int kMergeBatch = 16;
+  const Partial* P = a.part + (size_t)i * a.n_split;
+  const int d0 = slab * 16 + grp * 4;
+  float m[kMergeBatch], l[kMergeBatch], le[kMergeBatch], v[kMergeBatch][4];
+  auto load_batch = [&](int s0, int n) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (u < n) {
+        m[u] = P[s0 + u].m[h];
+        l[u] = P[s0 + u].l[h];
+        le[u] = P[s0 + u].le[h];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[u][r] = P[s0 + u].o[(d0 + r) * kHeads + h];
+      }
+    }
+  };
+  load_batch(0, min(kMergeBatch, a.n_split));
   int64_t base;
   int t;
   const bool valid = query_desc(a.b, i, base, t) && !(a.plan_miss != nullptr && a.plan_miss[i] != 0);
   OutT* out = static_cast<OutT*>(a.out) + (size_t)i * kHeads * kDim;
-  const int d0 = slab * 16 + grp * 4;
   if (!valid) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[h * kDim + d0 + r] = (OutT)NAN;
@@ -89,27 +108,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   const int n_keys = logical_keys(a.gather != 0, t, a.window, a.top_k);
   const int nv = min(a.n_split, (n_keys + a.split_keys - 1) / a.split_keys);
-  const Partial* P = a.part + (size_t)i * a.n_split;
   MergeAcc acc;
-  int s2 = 0;
-  for (; s2 + 4 <= nv; s2 += 4) {
-    float m[4], l[4], le[4], v[4][4];
+  for (int s0 = 0; s0 < nv; s0 += kMergeBatch) {
+    const int n = min(kMergeBatch, nv - s0);
+    if (s0 > 0) load_batch(s0, n);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      m[u] = P[s2 + u].m[h];
-      l[u] = P[s2 + u].l[h];
-      le[u] = P[s2 + u].le[h];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[u][r] = P[s2 + u].o[(d0 + r) * kHeads + h];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc.add(m[u], l[u], le[u], v[u]);
-  }
-  for (; s2 < nv; ++s2) {
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = P[s2].o[(d0 + r) * kHeads + h];
-    acc.add(P[s2].m[h], P[s2].l[h], P[s2].le[h], v);
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (u < n) acc.add(m[u], l[u], le[u], v[u]);
   }
   if (slab == 0 && grp == 0) {
     const float l2 = acc.m + __log2f(acc.le);
