@@ -140,6 +140,17 @@ def test_workspace_sizes_grow_with_the_batch(lib):
     assert lib.hs2_full_attn_select_workspace_size(None, 64, 128, 128, 1024, 0) == 0
 
 
+def test_sparse_workspace_of_many_query_batches_is_empty(lib):
+    """bf16 / FP8 sparse layers of at least two queries per CU (512) take one workgroup per
+    query with no split partials: no workspace; below that the keys are split and the
+    partials need one."""
+    for dt in (hs2.HS2_BF16, hs2.HS2_FP8_E4M3):
+        few = _batch(total_q=511, max_kv_len=8192, rows=8192, num_seqs=1)
+        many = _batch(total_q=512, max_kv_len=8192, rows=8192, num_seqs=1)
+        assert lib.hs2_sparse_attn_workspace_size(ctypes.byref(few), 64, 128, 128, 1024, dt) > 0
+        assert lib.hs2_sparse_attn_workspace_size(ctypes.byref(many), 64, 128, 128, 1024, dt) == 0
+
+
 def test_workspace_sizes_follow_host_lengths(lib):
     """Ragged single-query batches with a host copy of the lengths are planned from those
     lengths: the selector's workspace (per-split partials) differs from the equal-length
