@@ -66,9 +66,14 @@ __device__ inline uint32_t excl_scan256(uint32_t v, uint32_t* s_wave, uint32_t& 
 }
 
 // Q-tile list: (first query, count <= kQT) per tile, in sequence order; unused entries
-// get count 0. One workgroup of 256 threads.
+// get count 0. One workgroup of 256 threads. Sequences are taken 256 at a time; the
+// tiles of those sequences are then written by the whole workgroup, each thread finding
+// the sequence of its tile by binary search over the scanned tile offsets (a single
+// sequence of 262,144 queries has 65,536 tiles).
 __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles, int max_tiles) {
   __shared__ uint32_t s_wave[4];
+  __shared__ uint32_t s_pre[256];
+  __shared__ int s_q0[256], s_nq[256];
   uint32_t off = 0;
   for (int s0 = 0; s0 < b.num_seqs; s0 += 256) {
     const int s = s0 + threadIdx.x;
@@ -80,11 +85,25 @@ __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles,
     const uint32_t cnt = (uint32_t)((nq + kQT - 1) / kQT);
     uint32_t total;
     const uint32_t pre = excl_scan256(cnt, s_wave, total);
-    for (uint32_t j = 0; j < cnt; ++j) {
-      const uint32_t tix = off + pre + j;
-      if (tix < (uint32_t)max_tiles) tiles[tix] = make_int2(q0 + (int)j * kQT, min(kQT, nq - (int)j * kQT));
+    s_pre[threadIdx.x] = pre;
+    s_q0[threadIdx.x] = q0;
+    s_nq[threadIdx.x] = nq;
+    __syncthreads();
+    for (uint32_t t = threadIdx.x; t < total; t += 256) {
+      // The last sequence whose first tile is at or before t owns it: a sequence with
+      // no tiles shares its offset with the next one, and those at the end have offset
+      // `total`, so neither is picked.
+      int lo = 0, hi = 255;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int j = (int)(t - s_pre[lo]);
+      const uint32_t tix = off + t;
+      if (tix < (uint32_t)max_tiles) tiles[tix] = make_int2(s_q0[lo] + j * kQT, min(kQT, s_nq[lo] - j * kQT));
     }
     off += total;
+    __syncthreads();  // the next 256 sequences overwrite the shared offsets
   }
   for (uint32_t tix = off + threadIdx.x; tix < (uint32_t)max_tiles; tix += 256) tiles[tix] = make_int2(0, 0);
 }
