@@ -69,7 +69,7 @@ __device__ inline uint32_t excl_scan256(uint32_t v, uint32_t* s_wave, uint32_t& 
 // get count 0. One workgroup of 256 threads. Sequences are taken 256 at a time; the
 // tiles of those sequences are then written by the whole workgroup, each thread finding
 // the sequence of its tile by binary search over the scanned tile offsets (a single
-// sequence of 262,144 queries has 65,536 tiles).
+// sequence of 262,144 queries has 32,768 tiles).
 __global__ __launch_bounds__(256) void qtile_prep_kernel(SeqsDev b, int2* tiles, int max_tiles) {
   __shared__ uint32_t s_wave[4];
   __shared__ uint32_t s_pre[256];

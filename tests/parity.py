@@ -12,6 +12,11 @@ Comparison rules:
     ulp_bf16(fp64)/2): V's scale makes V's values non-representable in bf16, so even a
     query with a single attended key (out = v_0) carries the bf16 rounding of |v| ~ 1
     (mean ~1.1e-3), which a bf16 cache never has. The max rule is unchanged.
+    A query that attends at most FEW_KEYS keys has both its max and its mean taken beyond
+    each element's own output rounding: its output mixes two to four unit-scale V rows,
+    and their exact mix rounded to bf16 already has a mean error of up to 1.01e-3 over
+    64 x 128 values and a max of up to 1.02e-2 (an element of magnitude 4.3, where half a
+    bf16 unit is 1.6e-2), so the plain rules would reject the exact result.
   * LSE: |gpu - fp64| <= 1e-3 (fp32 output of a value of magnitude ~10).
 """
 from __future__ import annotations
@@ -26,6 +31,7 @@ REL_BAND = 1e-5
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 LSE_ABS = 1e-3
+FEW_KEYS = 4      # attended keys up to which the mean is taken beyond output rounding
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -65,11 +71,17 @@ def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 8.0)
 
 
-def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = "", beyond_rounding: bool = False):
+def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = "", beyond_rounding: bool = False,
+               few_keys: bool = False):
+    """beyond_rounding: the mean rule over the error beyond output rounding (FP8 K/V);
+    few_keys: the max and the mean rules over it (a query attending <= FEW_KEYS keys)."""
     err = np.abs(gpu - ref)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
-    assert err.max() <= MAX_ABS, f"{what}: max abs err {err.max():.3e}"
-    m = np.maximum(0.0, err - half_ulp_bf16(ref)) if beyond_rounding else err
+    beyond = np.maximum(0.0, err - half_ulp_bf16(ref))
+    mx = beyond if few_keys else err
+    assert mx.max() <= MAX_ABS, f"{what}: max abs err {mx.max():.3e}" + (" beyond rounding" if few_keys else "")
+    beyond_rounding = beyond_rounding or few_keys
+    m = beyond if beyond_rounding else err
     assert m.mean() <= MEAN_ABS, f"{what}: mean abs err {m.mean():.3e}" + (" beyond rounding" if beyond_rounding else "")
     return float(err.max()), float(m.mean())
 

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from long_context_mqa_amd import hs2
-from tests.parity import (check_attn, check_lse, check_selection, from_dev, oracle_query, oracle_sparse,
-                          to_dev)
+from tests.parity import (FEW_KEYS, check_attn, check_lse, check_selection, from_dev, oracle_query,
+                          oracle_sparse, to_dev)
 from workloads.configs import BlockSpec, block_config, make_block_inputs, make_bridge_inputs
 from workloads.gen import bf16_round, bf16_to_f32, e4m3_encode, stored_to_f64
 
@@ -63,12 +63,13 @@ def check_queries(inp, g, qis, what):
         t = r["t"]
         nc = oracle.candidate_count(t, sp.window)
         tag = f"{what} q{qi} t={t}"
-        check_attn(g["out"][qi], r["out"], tag + " selector out", beyond_rounding=rr)
+        few = t + 1 <= FEW_KEYS   # every layer of such a query attends all t + 1 keys
+        check_attn(g["out"][qi], r["out"], tag + " selector out", beyond_rounding=rr, few_keys=few)
         check_lse(g["lse"][qi], r["lse"], tag)
         swapped += check_selection(g["sel"][qi], int(g["count"][qi]), r, sp.top_k, nc, tag)
         for l, o in enumerate(g["sparse"]):
             ref, _ = oracle_sparse(inp, qi, l, g["sel"][qi], r["K"], r["V"])
-            check_attn(o[qi], ref, tag + f" sparse layer {l}", beyond_rounding=rr)
+            check_attn(o[qi], ref, tag + f" sparse layer {l}", beyond_rounding=rr, few_keys=few)
     return swapped
 
 
@@ -170,7 +171,8 @@ def test_sparse_layer_many_queries(dtype):
     rr = dtype == "fp8"
     for qi in range(spec.total_q):
         ref, _ = oracle_sparse(inp, qi, 0, g["sel"][qi])
-        check_attn(g["sparse"][0][qi], ref, f"many-queries q{qi} sparse", beyond_rounding=rr)
+        few = int(inp.q_pos[qi]) + 1 <= FEW_KEYS
+        check_attn(g["sparse"][0][qi], ref, f"many-queries q{qi} sparse", beyond_rounding=rr, few_keys=few)
     check_queries(inp, g, range(0, spec.total_q, 26), f"many-queries-{dtype}")
 
 
@@ -523,7 +525,7 @@ def _causal_check(spec, qis, what):
         a, t = int(inp.kv_start[s]), int(inp.q_pos[qi])
         ref, ref_lse, _ = oracle.full_attention(stored_to_f64(inp.q_sel[qi]), stored_to_f64(inp.k[a:a + t + 1]),
                                                 stored_to_f64(inp.v[a:a + t + 1]), t, spec.scale)
-        check_attn(o[qi], ref, f"causal {what} q{qi} t={t}")
+        check_attn(o[qi], ref, f"causal {what} q{qi} t={t}", few_keys=t + 1 <= FEW_KEYS)
         check_lse(lse[qi], ref_lse, f"causal {what} q{qi} t={t}")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
 
@@ -547,6 +549,26 @@ def test_causal_split_keys():
     spec = BlockSpec("causal-decode-split", [40000, 30000], [[39999, 20000, 5], [29999, 128, 0]], n_sparse=0,
                      needles_per_query=0, seed=27)
     _causal_check(spec, range(6), "decode-split")
+
+
+def test_causal_many_sequences():
+    """More sequences than one workgroup lists at a time (300 > 256) on the q-tile path:
+    sequences with no query, with every position a query and with query counts that are
+    not multiples of the tile size; every query against the oracle."""
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 61, 300)]
+    qpos = []
+    for si, n in enumerate(lens):
+        if si % 7 == 3:
+            qpos.append([])
+        elif si % 5 == 0:
+            qpos.append(list(range(n)))
+        else:
+            m = int(rng.integers(1, min(n, 11) + 1))
+            qpos.append(sorted(int(x) for x in rng.choice(n, m, replace=False)))
+    assert max(len(p) for p in qpos) >= 8          # at least one sequence takes q-tiles
+    spec = BlockSpec("causal-many-seqs", lens, qpos, n_sparse=0, needles_per_query=0, seed=42)
+    _causal_check(spec, range(spec.total_q), "many-seqs")
 
 
 def test_workload7_prefill_262144():
