@@ -137,6 +137,20 @@ def test_ragged_small_contexts(dtype):
     check_all_queries_properties(inp, g)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+def test_few_key_queries(dtype):
+    """Decode-shaped selector and sparse layers on queries that attend one to five keys
+    (t = 0..4), next to longer ones in the same batch."""
+    spec = BlockSpec("few-keys", [2, 3, 4, 5, 6, 50, 2000],
+                     [[1], [2, 0], [3, 1], [4, 2], [5, 3, 1], [1, 2, 3, 49], [4, 1999]],
+                     dtype=dtype, n_sparse=1, needles_per_query=0, seed=43)
+    inp = make_block_inputs(spec)
+    _say(f"few-key queries {dtype}")
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), f"few-keys-{dtype}")
+    check_all_queries_properties(inp, g)
+
+
 def test_chunked_ragged_queries():
     """Many queries per sequence (the q-tile kernels): query counts not multiples of the
     tile size, queries with t < window and with at most k candidates in the same tile."""
