@@ -141,6 +141,34 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _expect(name: str, t, dtypes, inner: tuple, min_rows: int, device=None) -> None:
+    """Rejects a tensor that the library would read or write through its plain pointer with
+    another element type, row length or row count than the entry point assumes (the C ABI
+    sees no buffer sizes, so a mismatch would be an out-of-bounds access on the device)."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {', '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape[1:]) != tuple(inner) or t.dim() != 1 + len(inner):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [rows, {', '.join(map(str, inner))}]")
+    if t.shape[0] < min_rows:
+        raise ValueError(f"{name}: {t.shape[0]} rows, the batch addresses {min_rows}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_attn_args(batch: "Batch", q, k, v, kv_dtypes, q_dtypes=(torch.bfloat16, torch.float32),
+                     kv_inner=(128,), out=None, lse=None) -> None:
+    """Q [total_q, 64, 128], K and V [total_kv_rows, *kv_inner], outputs like Q / [total_q, 64]."""
+    _expect("q", q, q_dtypes, (64, 128), batch.total_q)
+    _expect("k", k, kv_dtypes, kv_inner, batch.total_kv_rows, q.device)
+    _expect("v", v, kv_dtypes, kv_inner, batch.total_kv_rows, q.device)
+    _expect("out", out, (q.dtype,), (64, 128), batch.total_q, q.device)
+    _expect("lse", lse, (torch.float32,), (64,), batch.total_q, q.device)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -221,6 +249,9 @@ def full_attn_select(batch: Batch, q, k, v, window: int = 128, top_k: int = 1024
     """
     lib = load()
     dt = _dtype_code(q)
+    _check_attn_args(batch, q, k, v, (q.dtype,), out=out, lse=lse)
+    _expect("sel_idx", sel_idx, (torch.int32,), (max(top_k, 0),), batch.total_q, q.device)
+    _expect("sel_count", sel_count, (torch.int32,), (), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     dev = q.device
     if out is None:
@@ -248,6 +279,8 @@ def sparse_attn(batch: Batch, q, k, v, sel_idx, window: int = 128, top_k: int | 
     dt = _dtype_code(q)
     if top_k is None:
         top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    _check_attn_args(batch, q, k, v, (q.dtype,), out=out, lse=lse)
+    _expect("sel_idx", sel_idx if top_k > 0 else None, (torch.int32,), (top_k,), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     if out is None:
         out = torch.empty_like(q)
@@ -272,6 +305,8 @@ def sparse_attn_noalloc(batch: Batch, q, k, v, sel_idx, window: int = 128, top_k
     dt = _dtype_code(q)
     if top_k is None:
         top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    _check_attn_args(batch, q, k, v, (q.dtype,), out=out, lse=lse)
+    _expect("sel_idx", sel_idx if top_k > 0 else None, (torch.int32,), (top_k,), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     if out is None:
         out = torch.empty_like(q)
@@ -289,6 +324,15 @@ def bridge_kv(hidden, w_k: list, w_v: list, k_out: list | None = None, v_out: li
     n_rows, d_model = hidden.shape
     L = len(w_k)
     head_dim = w_k[0].shape[1]
+    _expect("hidden", hidden, (torch.bfloat16,), (d_model,), n_rows)
+    if len(w_v) != L or (k_out is not None and len(k_out) != L) or (v_out is not None and len(v_out) != L):
+        raise ValueError("w_k, w_v, k_out and v_out must hold one tensor per layer")
+    for name, ts in (("w_k", w_k), ("w_v", w_v)):
+        for t in ts:
+            _expect(name, t, (hidden.dtype,), (head_dim,), d_model, hidden.device)
+    for name, ts in (("k_out", k_out or []), ("v_out", v_out or [])):
+        for t in ts:
+            _expect(name, t, (hidden.dtype,), (head_dim,), n_rows, hidden.device)
     if k_out is None:
         k_out = [torch.empty(n_rows, head_dim, dtype=hidden.dtype, device=hidden.device) for _ in range(L)]
     if v_out is None:
@@ -334,6 +378,9 @@ def full_attn_select_fp8kv(batch: Batch, q, k, v, k_scale: float, v_scale: float
     if q.dtype != torch.bfloat16:
         raise TypeError("q must be bfloat16")
     k, v = _fp8_codes(k), _fp8_codes(v)
+    _check_attn_args(batch, q, k, v, (k.dtype,), q_dtypes=(torch.bfloat16,), out=out, lse=lse)
+    _expect("sel_idx", sel_idx, (torch.int32,), (max(top_k, 0),), batch.total_q, q.device)
+    _expect("sel_count", sel_count, (torch.int32,), (), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     dev = q.device
     if out is None:
@@ -365,6 +412,8 @@ def sparse_attn_fp8kv(batch: Batch, q, k, v, k_scale: float, v_scale: float, sel
     k, v = _fp8_codes(k), _fp8_codes(v)
     if top_k is None:
         top_k = sel_idx.shape[1] if sel_idx is not None else 0
+    _check_attn_args(batch, q, k, v, (k.dtype,), q_dtypes=(torch.bfloat16,), out=out, lse=lse)
+    _expect("sel_idx", sel_idx if top_k > 0 else None, (torch.int32,), (top_k,), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     if out is None:
         out = torch.empty_like(q)
@@ -390,6 +439,7 @@ def causal_attn(batch: Batch, q, k, v, scale: float | None = None, out=None, lse
     Returns (out [total_q, 64, 128], lse [total_q, 64] or None)."""
     lib = load()
     dt = _dtype_code(q)
+    _check_attn_args(batch, q, k, v, (q.dtype,), out=out, lse=lse)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     if out is None:
         out = torch.empty_like(q)
@@ -417,6 +467,15 @@ def bridge_kv_append(h, rows, w_k, w_v, k_cache, v_cache, workspace=None, stream
     assert rows.dtype == torch.int64 and rows.numel() == n_new
     cache_rows = int(k_cache[0].shape[0])
     assert all(int(c.shape[0]) == cache_rows for c in list(k_cache) + list(v_cache))
+    _expect("h", h, (torch.bfloat16,), (d_model,), n_new)
+    if len(w_v) != n_layers or len(k_cache) != n_layers or len(v_cache) != n_layers:
+        raise ValueError("w_k, w_v, k_cache and v_cache must hold one tensor per layer")
+    for name, ts in (("w_k", w_k), ("w_v", w_v)):
+        for t in ts:
+            _expect(name, t, (torch.bfloat16,), (128,), d_model, h.device)
+    for name, ts in (("k_cache", k_cache), ("v_cache", v_cache)):
+        for t in ts:
+            _expect(name, t, (torch.bfloat16,), (128,), cache_rows, h.device)
     arr = ctypes.c_void_p * n_layers
     need = lib.hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, 128)
     if workspace is None:
@@ -449,6 +508,8 @@ def v1_full_attn_select(batch: Batch, q, k, v, top_blocks: int = 16, scale: floa
     blk_count [total_q, 4]).
     """
     lib = load()
+    _check_attn_args(batch, q, k, v, (q.dtype,), q_dtypes=(torch.bfloat16,), kv_inner=(V1_KV_HEADS, 128), out=out,
+                     lse=lse)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     dev = q.device
     if out is None:
@@ -483,6 +544,10 @@ def v1_sparse_attn(batch: Batch, q, k, v, blk_idx, k_swa, v_swa, gate_sparse, ga
     gates [total_q, 64]. Returns out [total_q, 64, 128]."""
     lib = load()
     top_blocks = blk_idx.shape[-1]
+    _check_attn_args(batch, q, k, v, (q.dtype,), q_dtypes=(torch.bfloat16,), kv_inner=(V1_KV_HEADS, 128), out=out)
+    _expect("blk_idx", blk_idx, (torch.int32,), (V1_KV_HEADS, top_blocks), batch.total_q, q.device)
+    for name, t in (("gate_sparse", gate_sparse), ("gate_swa", gate_swa)):
+        _expect(name, t, (torch.float32,), (64,), batch.total_q, q.device)
     scale = float(scale if scale is not None else q.shape[-1] ** -0.5)
     if out is None:
         out = torch.empty_like(q)
