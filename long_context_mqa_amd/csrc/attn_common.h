@@ -136,6 +136,36 @@ __device__ inline void issue_tile(const void* __restrict__ src, int64_t base, in
   }
 }
 
+// The same copies for a contiguous tile: keys p0 .. p0+31 of the sequence whose first row
+// is `base`; a key at or past `pend` (not attended) copies row `base` instead, as
+// tile_rows' row 0 does. Each lane computes its rows' addresses itself.
+template <typename Kv, bool kIsK>
+__device__ inline void issue_tile_contig(const void* __restrict__ src, int64_t base, int p0, int pend, int lane,
+                                         uint32_t lds) {
+  wait_lgkm0();
+  if constexpr (!Kv::kFp8) {
+    const __bf16* s = static_cast<const __bf16*>(src);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = r * 4 + (lane >> 4);
+      const int p = p0 + row;
+      const int rel = p < pend ? p : 0;
+      const int chunk = kIsK ? ((lane & 15) ^ (row & 15)) : v_chunk(row, lane & 15);
+      dma16(s + (base + rel) * kDim + chunk * 8, lds + r * 1024);
+    }
+  } else {
+    const uint8_t* s8 = static_cast<const uint8_t*>(src);
+#pragma unroll
+    for (int r = 0; r < Kv::kDma; ++r) {
+      const int row = r * 8 + (lane >> 3);
+      const int p = p0 + row;
+      const int rel = p < pend ? p : 0;
+      const int chunk = (lane & 7) ^ (kIsK ? k8_swz(row) : v8_swz(row));
+      dma16(s8 + (base + rel) * Kv::kRowBytes + chunk * 16, lds + r * 1024);
+    }
+  }
+}
+
 // Online-softmax state of one wave: 64 heads x 128 dims, O^T in the C layout.
 // The softmax reference m of a head is fixed at the first tile that holds an attended
 // key (that tile's maximum); later tiles are not rescaled. exp2(x - m) may then exceed 1,

@@ -47,8 +47,9 @@ struct AttnSmem {
 // its PV step, so S tiles stream in while one is computed. Waits count the copies issued
 // later: constant in the steady state, and in the last S tiles a compile-time count per
 // tile (the tail is unrolled), so the loop has no branches around its waits. The mask of
-// attended keys is recomputed when a tile is processed (no per-stage state). kMaxOnly:
-// only the logit maximum of the attended keys (into mx).
+// attended keys is recomputed when a tile is processed (no per-stage state); the copies
+// take their rows straight from the tile's first key (the keys are contiguous), with no
+// exchange between lanes. kMaxOnly: only the logit maximum of the attended keys (into mx).
 template <typename Kv, int kW, bool kMaxOnly, int kLater, bool kMore>
 __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& sm, const KeyList& kl, int k0, int k1,
                                    const void* __restrict__ kp, const void* __restrict__ vp, float c2, int wave,
@@ -59,12 +60,11 @@ __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& 
   const uint8_t* kt = sm.stage[wave] + (2 * sidx) * T;
   bf16x8 kop[8];
   read_k_of<Kv>(kt, lane, kop);
-  int rel;
+  int rel;  // unused here: the copies compute their rows from the tile's first key
   const uint32_t vm = tile_rows(kl, k0 + ord.at(wave + it * kW) * kTile, k1, lane, rel);
-  if (kMore) {
-    tile_rows(kl, k0 + ord.at(wave + (it + S) * kW) * kTile, k1, lane, rel);
-    issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * sidx) * T);
-  }
+  const int pend = min(k1, kl.n_keys);                                  // keys past it copy row 0
+  const int pn = kMore ? k0 + ord.at(wave + (it + S) * kW) * kTile : 0;  // first key of tile it+S
+  if (kMore) issue_tile_contig<Kv, true>(kp, kl.base, pn, pend, lane, wbase + (2 * sidx) * T);
   wait_vmcnt<D * (2 * kLater + (kMore ? 1 : 0))>();  // V(it) has landed
   if (vm != 0u) {
     if (kMaxOnly)
@@ -72,7 +72,7 @@ __device__ inline void stream_step(WaveState& st, float (&mx)[2], AttnSmem<kW>& 
     else
       process_tile<false, Kv>(st, sm.q, nullptr, kop, kt + T, vb, vm, c2, lane);
   }
-  if (kMore) issue_tile<Kv, false>(vp, kl.base, rel, lane, wbase + (2 * sidx + 1) * T);
+  if (kMore) issue_tile_contig<Kv, false>(vp, kl.base, pn, pend, lane, wbase + (2 * sidx + 1) * T);
 }
 
 template <typename Kv, int kW, bool kMaxOnly, int kLater>
@@ -95,10 +95,9 @@ __device__ inline void stream_tiles(WaveState& st, float (&mx)[2], AttnSmem<kW>&
   uint32_t vb[4];
   vt_bases_of<Kv>(lane, vb);
   for (int it = 0; it < min(ntw, S); ++it) {
-    int rel;
-    tile_rows(kl, k0 + ord.at(wave + it * kW) * kTile, k1, lane, rel);
-    issue_tile<Kv, true>(kp, kl.base, rel, lane, wbase + (2 * it) * T);
-    issue_tile<Kv, false>(vp, kl.base, rel, lane, wbase + (2 * it + 1) * T);
+    const int p0 = k0 + ord.at(wave + it * kW) * kTile, pend = min(k1, kl.n_keys);
+    issue_tile_contig<Kv, true>(kp, kl.base, p0, pend, lane, wbase + (2 * it) * T);
+    issue_tile_contig<Kv, false>(vp, kl.base, p0, pend, lane, wbase + (2 * it + 1) * T);
   }
   for (int it = 0; it + S < ntw; ++it)
     stream_step<Kv, kW, kMaxOnly, S - 1, true>(st, mx, sm, kl, k0, k1, kp, vp, c2, wave, lane, vb, wbase, ord, it);

@@ -138,9 +138,8 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
   auto tile_of = [&](int x) { return ord.at(ntiles - 1 - x); };
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
   auto issue = [&](int it, int sidx) {
-    const int p = k0 + tile_of(wave + it * kSWaves) * kTile + (lane & 31);
-    const int rel = p < k1 ? p : 0;
-    issue_tile<Kv, true>(a.k, base, rel, lane, wbase + sidx * Kv::kTileBytes);
+    issue_tile_contig<Kv, true>(a.k, base, k0 + tile_of(wave + it * kSWaves) * kTile, k1, lane,
+                                wbase + sidx * Kv::kTileBytes);
   };
   for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, it);
   for (int it = 0; it < ntw; ++it) {
