@@ -138,7 +138,8 @@ __device__ inline void issue_tile(const void* __restrict__ src, int64_t base, in
 
 // The same copies for a contiguous tile: keys p0 .. p0+31 of the sequence whose first row
 // is `base`; a key at or past `pend` (not attended) copies row `base` instead, as
-// tile_rows' row 0 does. Each lane computes its rows' addresses itself.
+// tile_rows' row 0 does. Each lane computes its rows' addresses itself. The decode passes
+// read each of these rows once, so the copies are marked non-temporal.
 template <typename Kv, bool kIsK>
 __device__ inline void issue_tile_contig(const void* __restrict__ src, int64_t base, int p0, int pend, int lane,
                                          uint32_t lds) {
@@ -151,7 +152,7 @@ __device__ inline void issue_tile_contig(const void* __restrict__ src, int64_t b
       const int p = p0 + row;
       const int rel = p < pend ? p : 0;
       const int chunk = kIsK ? ((lane & 15) ^ (row & 15)) : v_chunk(row, lane & 15);
-      dma16(s + (base + rel) * kDim + chunk * 8, lds + r * 1024);
+      dma16_nt(s + (base + rel) * kDim + chunk * 8, lds + r * 1024);
     }
   } else {
     const uint8_t* s8 = static_cast<const uint8_t*>(src);
@@ -161,7 +162,7 @@ __device__ inline void issue_tile_contig(const void* __restrict__ src, int64_t b
       const int p = p0 + row;
       const int rel = p < pend ? p : 0;
       const int chunk = (lane & 7) ^ (kIsK ? k8_swz(row) : v8_swz(row));
-      dma16(s8 + (base + rel) * Kv::kRowBytes + chunk * 16, lds + r * 1024);
+      dma16_nt(s8 + (base + rel) * Kv::kRowBytes + chunk * 16, lds + r * 1024);
     }
   }
 }

@@ -117,7 +117,8 @@ __device__ inline uint32_t tile_mask(const TileSrc& ts, int it, int lane) {
 
 // Enqueues the 32 rows of the K or V tile `it` into LDS in the swizzles of the MQA tiles
 // (copy r writes rows 4r .. 4r+3; lane l fills chunk position l%16 of row 4r + l/16).
-// Earlier LDS reads of the stage must have completed.
+// Earlier LDS reads of the stage must have completed. The selector pass reads each row
+// once (non-temporal copies); the sparse layers gather rows that later layers read again.
 template <int kMode, bool kIsK>
 __device__ inline void issue_v1(const TileSrc& ts, int it, int lane, uint32_t lds) {
   wait_lgkm0();
@@ -128,7 +129,10 @@ __device__ inline void issue_v1(const TileSrc& ts, int it, int lane, uint32_t ld
     bool ok;
     const int64_t row = key_row<kMode>(ts, it, kk, ok);
     const int chunk = kIsK ? ((lane & 15) ^ (kk & 15)) : v_chunk(kk, lane & 15);
-    dma16(src + row * kRowElems + chunk * 8, lds + r * 1024);
+    if constexpr (kMode == kModeFull)
+      dma16_nt(src + row * kRowElems + chunk * 8, lds + r * 1024);
+    else
+      dma16(src + row * kRowElems + chunk * 8, lds + r * 1024);
   }
 }
 
