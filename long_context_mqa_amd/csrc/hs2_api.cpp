@@ -199,7 +199,7 @@ SelectPlan plan_select(const hs2_seqs* b, int window, int top_k, hs2_dtype dt, b
     p.score_lists = !p.chunk && dt != HS2_F32;
     if (p.score_lists) {
       // per (query, score split, wave): up to all of the wave's candidates as 8-byte pairs
-      p.list_waves = dt == HS2_FP8_E4M3 ? 8 : 4;
+      p.list_waves = score_waves(dt == HS2_FP8_E4M3);  // one list per wave of the score pass
       p.list_cap = (int)(ceil_div(ceil_div(p.score.split_keys, kTile), p.list_waves) * kTile);
       const size_t nl = (size_t)tq * p.score.n_split * p.list_waves;
       p.off_lists = off;

@@ -7,6 +7,11 @@
 
 namespace hs2 {
 
+// Waves per workgroup of the decode-shaped score pass (4 for bf16 tiles, 8 for FP8 tiles).
+// Each wave keeps its own candidate list, so the kernel's launch shape and the planner's
+// list area are both sized from this one value.
+constexpr int score_waves(bool fp8) { return fp8 ? 8 : 4; }
+
 // Sets the calling thread's hs2_last_error() text and returns st (for entry points
 // defined outside hs2_api.cpp).
 hs2_status set_error(hs2_status st, const char* msg);

@@ -35,7 +35,7 @@ constexpr int kSBufTiles = 128;  // tiles of scores staged per workgroup before 
 // two waves per SIMD.
 template <typename Kv>
 struct ScoreCfg {
-  static constexpr int kSWaves = Kv::kFp8 ? 8 : 4;
+  static constexpr int kSWaves = score_waves(Kv::kFp8);
   static constexpr int kWaveBytes = kScoreStageBytes / kSWaves;
   static constexpr int kStages = kWaveBytes / Kv::kTileBytes;  // 4 bf16 or 4 FP8 tiles per wave
   static constexpr int kSFlush = kSBufTiles / kSWaves;          // tiles staged per wave
