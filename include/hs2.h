@@ -138,6 +138,26 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
                          size_t workspace_bytes, hs2_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * KV Bridging into FP8 caches: the same projections, written as the OCP FP8 E4M3 caches
+ * that the *_fp8kv entry points read ([arex] "Numbers computed on three 80B-A3B models"
+ * accounts the KV cache in FP8). With one scale per output tensor, element (r, c) of
+ * layer l's K cache is the E4M3 code nearest to (H W_K^l)[r][c] / k_scale[l] (ties to
+ * the even mantissa; magnitudes above 448 saturate to 448), and likewise for V.
+ *
+ *   hidden, w_k, w_v, workspace: as for hs2_bridge_kv (bf16, same workspace size)
+ *   k_out,   HOST arrays of n_layers DEVICE pointers, each [n_rows][head_dim] bytes of
+ *   v_out    E4M3 codes, 16-byte aligned
+ *   k_scale, HOST arrays of n_layers scales, each finite and > 0 (the value a code
+ *   v_scale  stands for is scale * its E4M3 value); the products are computed in fp32
+ *            as (H W)[r][c] * (1 / scale), then converted
+ *   Limits: as for hs2_bridge_kv. HS2_ERR_INVALID_ARG for a NULL array or a bad scale.
+ * ------------------------------------------------------------------------------------ */
+hs2_status hs2_bridge_kv_fp8kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                               const void* const* w_k, const void* const* w_v, void* const* k_out,
+                               void* const* v_out, const float* k_scale, const float* v_scale,
+                               int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Full-attention selector layer ([arex] "Outer KV Bridging, inner KV Reuse": the few
  * full-attention layers act as the indexer, with their exact attention scores;
  * [toolnavs] "Was HySparse2 tut"). For each query i at position t of sequence s:

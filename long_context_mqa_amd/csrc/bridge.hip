@@ -84,8 +84,8 @@ __device__ inline void wait_vm() {
 
 // kCols output columns per workgroup (256 or 384). Wave w: rows kWR*(w%kRW) .. of the
 // tile, columns kWC*(w/kRW) .., as kXB x kYB blocks of 32 x 32.
-template <int kCols>
-__global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a) {
+template <int kCols, bool kFp8Out>
+__global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a, BridgeOut o) {
   constexpr int kTA = kCols * kKStep * 2;        // W^T tile bytes per stage
   constexpr int kTB = kBM * kKStep * 2;          // H tile bytes per stage
   constexpr int kCopA = kCols / kRowsPerCopy / kGWaves;  // 1 KB copies per wave per stage
@@ -178,12 +178,20 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
   // Results through LDS, 128 rows at a time: the waves holding those rows write them as bf16
   // rows of kCols columns, then every store instruction writes four whole 256-byte rows of one
   // output matrix. C^T[n][row]: lane l holds rows 32 y + l % 32, columns 32 x + 8 jg + 4 (l / 32)
-  // + 0..3 of block (x, y).
-  constexpr int kPitch = kCols * 2 + 16;
+  // + 0..3 of block (x, y). FP8 output: the four values are scaled by their matrix's
+  // reciprocal scale, clamped to the largest E4M3 magnitude (448) and converted (round to
+  // nearest even) into one 32-bit word of codes; rows are then 128 bytes per matrix and each
+  // store instruction writes eight of them.
+  constexpr int kEB = kFp8Out ? 1 : 2;                 // bytes per output element
+  constexpr int kPitch = kCols * kEB + 16;
   static_assert(128 * kPitch <= kStagesG * (kTA + kTB), "a half tile fits in the stage area");
   uint8_t* epi = lds_all;  // the stage area, free once every wave is past the last stage
   const int last = (int)(a.n_rows - r0 < kBM ? a.n_rows - r0 : kBM) - 1;
-  constexpr int kSegs = 128 / 4 * (kCols / kDim);  // 1 KB stores per half tile
+  constexpr int kRowsPerStore = 1024 / (kDim * kEB);   // whole output rows per store instruction
+  constexpr int kLanesPerRowOut = 64 / kRowsPerStore;
+  constexpr int kSegsPerMat = 128 / kRowsPerStore;
+  constexpr int kSegs = kSegsPerMat * (kCols / kDim);  // 1 KB stores per half tile
+  static_assert(kSegs % kGWaves == 0, "stores must split evenly");
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();  // stage reads (or the previous half's stores) are done
@@ -194,24 +202,36 @@ __global__ __launch_bounds__(64 * kGWaves) void bridge_gemm_kernel(BridgeArgs a)
         for (int x = 0; x < kXB; ++x)
 #pragma unroll
           for (int jg = 0; jg < 4; ++jg) {
-            __bf16 v4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v4[q] = (__bf16)acc[x][y][4 * jg + q];
             const int row = wr * kWR - 128 * half + 32 * y + (lane & 31);
             const int col = wc * kWC + 32 * x + 8 * jg + 4 * (lane >> 5);
-            *reinterpret_cast<uint2*>(epi + row * kPitch + col * 2) = __builtin_bit_cast(uint2, v4);
+            if constexpr (kFp8Out) {
+              const float is = o.inv_scale[nt * (kCols / kDim) + col / kDim];  // this column's output matrix
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = fminf(fmaxf(acc[x][y][4 * jg + q] * is, -448.0f), 448.0f);
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+              w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+              *reinterpret_cast<int*>(epi + row * kPitch + col) = w;
+            } else {
+              __bf16 v4[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v4[q] = (__bf16)acc[x][y][4 * jg + q];
+              *reinterpret_cast<uint2*>(epi + row * kPitch + col * 2) = __builtin_bit_cast(uint2, v4);
+            }
           }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSegs / kGWaves; ++i) {
       const int idx = wave * (kSegs / kGWaves) + i;
-      const int m = idx / 32;                        // output matrix of the tile
-      const int row = (idx % 32) * 4 + (lane >> 4);  // row within the half
-      const uint4 v = *reinterpret_cast<const uint4*>(epi + row * kPitch + m * 256 + (lane & 15) * 16);
+      const int m = idx / kSegsPerMat;                                  // output matrix of the tile
+      const int row = (idx % kSegsPerMat) * kRowsPerStore + lane / kLanesPerRowOut;  // row within the half
+      const int chunk = lane % kLanesPerRowOut;                          // 16-byte chunk of the row
+      const uint4 v = *reinterpret_cast<const uint4*>(epi + row * kPitch + m * kDim * kEB + chunk * 16);
       const int trow = 128 * half + row;
       if (trow <= last)
-        *reinterpret_cast<uint4*>(a.outs[nt * (kCols / kDim) + m] + (r0 + trow) * kDim + (lane & 15) * 8) = v;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.outs[nt * (kCols / kDim) + m]) +
+                                  ((r0 + trow) * kDim + chunk * (16 / kEB)) * kEB) = v;
     }
   }
 }
@@ -228,16 +248,20 @@ hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w
   return hipGetLastError();
 }
 
-hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s) {
+hipError_t launch_bridge_gemm(const BridgeArgs& a, const BridgeOut& o, hipStream_t s) {
   const int64_t n_rt = (a.n_rows + kBM - 1) / kBM;
   const int64_t per_xcd = (n_rt + kXcds - 1) / kXcds;
-  if (a.n_mats % 3 == 0) {
-    const int64_t grid = per_xcd * kXcds * (a.n_mats * kDim / 384);
-    hipLaunchKernelGGL(bridge_gemm_kernel<384>, dim3((unsigned)grid), dim3(64 * kGWaves), 0, s, a);
-  } else {
-    const int64_t grid = per_xcd * kXcds * (a.n_mats * kDim / 256);
-    hipLaunchKernelGGL(bridge_gemm_kernel<256>, dim3((unsigned)grid), dim3(64 * kGWaves), 0, s, a);
-  }
+  const bool wide = a.n_mats % 3 == 0;
+  const int64_t grid = per_xcd * kXcds * (a.n_mats * kDim / (wide ? 384 : 256));
+  const dim3 g((unsigned)grid), b(64 * kGWaves);
+  if (wide && o.fp8)
+    hipLaunchKernelGGL((bridge_gemm_kernel<384, true>), g, b, 0, s, a, o);
+  else if (wide)
+    hipLaunchKernelGGL((bridge_gemm_kernel<384, false>), g, b, 0, s, a, o);
+  else if (o.fp8)
+    hipLaunchKernelGGL((bridge_gemm_kernel<256, true>), g, b, 0, s, a, o);
+  else
+    hipLaunchKernelGGL((bridge_gemm_kernel<256, false>), g, b, 0, s, a, o);
   return hipGetLastError();
 }
 

@@ -830,11 +830,15 @@ size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t h
   return align_up((size_t)2 * n_layers * head_dim * d_model * sizeof(uint16_t));
 }
 
-hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
-                         const void* const* w_k, const void* const* w_v, void* const* k_out,
-                         void* const* v_out, int32_t head_dim, void* workspace, size_t workspace_bytes,
-                         hs2_dtype dt, void* stream) {
-  if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "bridging supports bf16 only");
+}  // extern "C"
+
+namespace {
+
+// Both bridging entry points: bf16 outputs, or (k_scale and v_scale given) FP8 E4M3 codes.
+hs2_status bridge_impl(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                       const void* const* w_k, const void* const* w_v, void* const* k_out, void* const* v_out,
+                       const float* k_scale, const float* v_scale, int32_t head_dim, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "bridging supports head_dim=128 only (got %d)", head_dim);
   if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
     return fail(HS2_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 65536] (got %d)", d_model);
@@ -843,14 +847,27 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
   if (!w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARG, "pointer arrays must not be NULL");
   if (n_rows > 0 && !hidden) return fail(HS2_ERR_INVALID_ARG, "hidden must not be NULL");
   if (!aligned(hidden, 16)) return fail(HS2_ERR_INVALID_ARG, "hidden must be 16-byte aligned");
+  const bool fp8 = k_scale != nullptr;
   const uint16_t* w[16];
   BridgeArgs a{};
+  BridgeOut o{};
+  o.fp8 = fp8 ? 1 : 0;
   for (int l = 0; l < n_layers; ++l) {
     if (!w_k[l] || !w_v[l] || !k_out[l] || !v_out[l])
       return fail(HS2_ERR_INVALID_ARG, "a weight or output pointer of layer %d is NULL", l);
     if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_out[l], 16) || !aligned(v_out[l], 16))
       return fail(HS2_ERR_INVALID_ARG, "weights and outputs must be 16-byte aligned (layer %d)", l);
     if (k_out[l] == hidden || v_out[l] == hidden) return fail(HS2_ERR_INVALID_ARG, "an output aliases hidden");
+    if (fp8) {
+      const float ks = k_scale[l], vs = v_scale[l];
+      if (!(std::isfinite(ks) && ks > 0.0f && std::isfinite(vs) && vs > 0.0f))
+        return fail(HS2_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0 (layer %d)", l);
+      const float ik = 1.0f / ks, iv = 1.0f / vs;
+      if (!std::isfinite(ik) || !std::isfinite(iv))
+        return fail(HS2_ERR_INVALID_ARG, "the reciprocal of a scale overflows (layer %d)", l);
+      o.inv_scale[2 * l] = ik;
+      o.inv_scale[2 * l + 1] = iv;
+    }
     w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
     w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
     a.outs[2 * l] = static_cast<uint16_t*>(k_out[l]);
@@ -873,10 +890,32 @@ hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, in
   if (e != hipSuccess) return hip_fail(e, "bridging weight transpose launch");
   if (n_rows == 0) return ok();
   e = mk.before(1);
-  if (e == hipSuccess) e = launch_bridge_gemm(a, s);
+  if (e == hipSuccess) e = launch_bridge_gemm(a, o, s);
   if (e == hipSuccess) e = mk.after(1);
   if (e != hipSuccess) return hip_fail(e, "bridging launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_bridge_kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                         const void* const* w_k, const void* const* w_v, void* const* k_out,
+                         void* const* v_out, int32_t head_dim, void* workspace, size_t workspace_bytes,
+                         hs2_dtype dt, void* stream) {
+  if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "bridging supports bf16 only");
+  return bridge_impl(hidden, n_rows, d_model, n_layers, w_k, w_v, k_out, v_out, nullptr, nullptr, head_dim,
+                     workspace, workspace_bytes, stream);
+}
+
+hs2_status hs2_bridge_kv_fp8kv(const void* hidden, int64_t n_rows, int32_t d_model, int32_t n_layers,
+                               const void* const* w_k, const void* const* w_v, void* const* k_out,
+                               void* const* v_out, const float* k_scale, const float* v_scale, int32_t head_dim,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_scale || !v_scale) return fail(HS2_ERR_INVALID_ARG, "k_scale and v_scale must not be NULL");
+  return bridge_impl(hidden, n_rows, d_model, n_layers, w_k, w_v, k_out, v_out, k_scale, v_scale, head_dim,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

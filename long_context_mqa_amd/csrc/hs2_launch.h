@@ -42,7 +42,13 @@ hipError_t launch_topk_filter(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finish(const TopkArgs& a, hipStream_t s);
 hipError_t launch_bridge_transpose(const BridgeArgs& a, const uint16_t* const* w, int32_t n_mats,
                                    uint16_t* wt, hipStream_t s);
-hipError_t launch_bridge_gemm(const BridgeArgs& a, hipStream_t s);
+// Output form of the bridging GEMM: bf16 rows, or (fp8 set) OCP E4M3 codes of
+// min(max(value * inv_scale[m], -448), 448) for output matrix m, rows of 128 bytes.
+struct BridgeOut {
+  int32_t fp8;
+  float inv_scale[16];
+};
+hipError_t launch_bridge_gemm(const BridgeArgs& a, const BridgeOut& o, hipStream_t s);
 hipError_t launch_bridge_append(const AppendArgs& a, hipStream_t s);
 
 hipError_t launch_v1_attn(const V1AttnArgs& a, bool sparse, int grid, hipStream_t s);

@@ -27,6 +27,7 @@ EXPORTED = [
     "hs2_last_error",
     "hs2_bridge_kv_workspace_size",
     "hs2_bridge_kv",
+    "hs2_bridge_kv_fp8kv",
     "hs2_full_attn_select_workspace_size",
     "hs2_full_attn_select",
     "hs2_sparse_attn_workspace_size",
@@ -88,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_bridge_kv_workspace_size.argtypes = [I32, I32, I32]
     lib.hs2_bridge_kv.restype = I32
     lib.hs2_bridge_kv.argtypes = [P, I64, I32, I32, P, P, P, P, I32, P, SZ, I32, P]
+    lib.hs2_bridge_kv_fp8kv.restype = I32
+    lib.hs2_bridge_kv_fp8kv.argtypes = [P, I64, I32, I32, P, P, P, P, P, P, I32, P, SZ, P]
     lib.hs2_full_attn_select_workspace_size.restype = SZ
     lib.hs2_full_attn_select_workspace_size.argtypes = [SP, I32, I32, I32, I32, I32]
     lib.hs2_full_attn_select.restype = I32
@@ -347,6 +350,43 @@ def bridge_kv(hidden, w_k: list, w_v: list, k_out: list | None = None, v_out: li
         workspace = _workspace(need, hidden.device)
     _check(lib.hs2_bridge_kv(_ptr(hidden), n_rows, d_model, L, wk, wv, ko, vo, head_dim, _ptr(workspace),
                              workspace.numel(), _dtype_code(hidden), _stream(stream)))
+    return k_out, v_out
+
+
+def bridge_kv_fp8kv(hidden, w_k: list, w_v: list, k_scale, v_scale, k_out: list | None = None,
+                    v_out: list | None = None, workspace=None, stream=None):
+    """hs2_bridge_kv_fp8kv: the bridging projections written as FP8 E4M3 caches (uint8 codes
+    [n_rows, 128] per layer) with one scale per tensor; k_scale and v_scale are one float
+    for every layer or a list with one per layer."""
+    lib = load()
+    n_rows, d_model = hidden.shape
+    L = len(w_k)
+    head_dim = w_k[0].shape[1]
+    ks = [float(k_scale)] * L if isinstance(k_scale, (int, float)) else [float(x) for x in k_scale]
+    vs = [float(v_scale)] * L if isinstance(v_scale, (int, float)) else [float(x) for x in v_scale]
+    _expect("hidden", hidden, (torch.bfloat16,), (d_model,), n_rows)
+    if len(w_v) != L or len(ks) != L or len(vs) != L or (k_out is not None and len(k_out) != L) or \
+            (v_out is not None and len(v_out) != L):
+        raise ValueError("w_k, w_v, the scales, k_out and v_out must hold one entry per layer")
+    for name, ts in (("w_k", w_k), ("w_v", w_v)):
+        for t in ts:
+            _expect(name, t, (torch.bfloat16,), (head_dim,), d_model, hidden.device)
+    for name, ts in (("k_out", k_out or []), ("v_out", v_out or [])):
+        for t in ts:
+            _expect(name, t, (torch.uint8, torch.float8_e4m3fn), (head_dim,), n_rows, hidden.device)
+    if k_out is None:
+        k_out = [torch.empty(n_rows, head_dim, dtype=torch.uint8, device=hidden.device) for _ in range(L)]
+    if v_out is None:
+        v_out = [torch.empty(n_rows, head_dim, dtype=torch.uint8, device=hidden.device) for _ in range(L)]
+    arr = ctypes.c_void_p * L
+    farr = ctypes.c_float * L
+    need = lib.hs2_bridge_kv_workspace_size(d_model, L, head_dim)
+    if workspace is None:
+        workspace = _workspace(need, hidden.device)
+    _check(lib.hs2_bridge_kv_fp8kv(_ptr(hidden), n_rows, d_model, L, arr(*[w.data_ptr() for w in w_k]),
+                                   arr(*[w.data_ptr() for w in w_v]), arr(*[t.data_ptr() for t in k_out]),
+                                   arr(*[t.data_ptr() for t in v_out]), farr(*ks), farr(*vs), head_dim,
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
     return k_out, v_out
 
 

@@ -7,9 +7,11 @@ from .hs2_oracle import (  # noqa: F401
     attended_rows,
     block_query,
     bridge_kv,
+    bridge_kv_fp8,
     candidate_count,
     dequantize_kv,
     e4m3_decode,
+    e4m3_encode,
     full_attention,
     logits,
     select_topk,

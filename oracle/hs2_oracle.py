@@ -35,6 +35,9 @@ design notes of the repository):
   R8  an FP8 KV cache ([arex] "Numbers computed on three 80B-A3B models" accounts the
       KV cache in FP8; the format is not named) holds OCP FP8 E4M3 codes with one
       scale per tensor: row j stands for scale * decode(codes of row j).
+  R9  writing such a cache: the code of a value x is the E4M3 value nearest to
+      x / scale, ties to the even mantissa, with magnitudes above 448 saturated to 448
+      (the format has no infinities; the pages give no rounding rule).
 """
 from __future__ import annotations
 
@@ -56,6 +59,31 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
     mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
     return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes of float64 values (R9).
+
+    Each magnitude is rounded onto the E4M3 grid of its binade: [2^e, 2^(e+1)) for
+    e >= -6 holds the 8 values (1 + m/8) * 2^e, and below 2^-6 the subnormals (m/8) * 2^-6
+    share the step 2^-9 of the lowest binade. Halfway cases go to the even m (a value
+    that rounds up to 2^(e+1) becomes the first value of the next binade). Magnitudes
+    above 448 give 448; NaN gives 0x7F. The sign bit is kept, also for zero.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.where(np.isnan(x), 0.0, np.abs(x))
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))        # max(a, 2^-6) = f * 2^ex, f in [0.5, 1)
+    step = np.exp2(ex.astype(np.float64) - 1.0 - 3.0)  # binade 2^(ex-1), 3 mantissa bits
+    r = np.minimum(np.round(a / step) * step, 448.0)   # numpy rounds halves to even
+    _, er = np.frexp(np.maximum(r, 2.0 ** -6))
+    er = er.astype(np.int64) - 1                       # binade of the rounded value
+    normal = r >= 2.0 ** -6
+    e_field = np.where(normal, er + 7, 0)
+    m_field = np.where(normal, r / np.exp2(er.astype(np.float64)) * 8.0 - 8.0, r / 2.0 ** -9)
+    code = (e_field << 3) | np.rint(m_field).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
 
 
 def dequantize_kv(codes: np.ndarray, scale: float) -> np.ndarray:
@@ -161,6 +189,14 @@ def bridge_kv(H: np.ndarray, w_k: list, w_v: list):
     one hidden-state source may feed several layers.
     """
     return [H @ w for w in w_k], [H @ w for w in w_v]
+
+
+def bridge_kv_fp8(H: np.ndarray, w_k: list, w_v: list, k_scales: list, v_scales: list):
+    """KV Bridging into FP8 caches (R7, R8, R9): layer l's K cache holds the E4M3 codes
+    of (H @ W_K^l) / k_scales[l], its V cache those of (H @ W_V^l) / v_scales[l]."""
+    ks, vs = bridge_kv(H, w_k, w_v)
+    return ([e4m3_encode(k / float(s)) for k, s in zip(ks, k_scales)],
+            [e4m3_encode(v / float(s)) for v, s in zip(vs, v_scales)])
 
 
 def selector_query(q_sel: np.ndarray, K: np.ndarray, V: np.ndarray, t: int, window: int,

@@ -129,6 +129,29 @@ def test_bridge_rejects_bad_arguments(lib):
     assert call(ws=ws - 2) == hs2.HS2_ERR_WORKSPACE
 
 
+def test_fp8_bridge_rejects_bad_arguments(lib):
+    """The FP8-output bridging checks everything hs2_bridge_kv checks, plus its scales."""
+    P = ctypes.c_void_p * 3
+    F = ctypes.c_float * 3
+    w = P(FAKE, FAKE, FAKE)
+    o = P(FAKE * 2, FAKE * 3, FAKE * 4)
+    ws = lib.hs2_bridge_kv_workspace_size(2048, 3, 128)
+    good = F(0.05, 0.05, 0.05)
+
+    def call(ks=good, vs=good, ws_bytes=ws, hd=128, n=1000):
+        return lib.hs2_bridge_kv_fp8kv(FAKE * 5, n, 2048, 3, w, w, o, o, ks, vs, hd, FAKE * 8, ws_bytes, None)
+    assert call(ks=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(vs=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ks=F(0.05, 0.0, 0.05)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(vs=F(0.05, 0.05, -1.0)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ks=F(0.05, float("inf"), 0.05)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ks=F(0.05, float("nan"), 0.05)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(vs=F(1e-45, 0.05, 0.05)) == hs2.HS2_ERR_INVALID_ARG   # reciprocal overflows
+    assert call(hd=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(n=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 2) == hs2.HS2_ERR_WORKSPACE
+
+
 def test_workspace_sizes_grow_with_the_batch(lib):
     small = _batch(total_q=4, max_kv_len=8192, rows=8192 * 4, num_seqs=4)
     big = _batch(total_q=64, max_kv_len=131072, rows=131072 * 64, num_seqs=64)

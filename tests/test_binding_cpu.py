@@ -104,3 +104,13 @@ def test_v1_cache_layout():
     k = torch.zeros(600, 128, dtype=torch.bfloat16)      # an MQA cache, not [rows, 4, 128]
     with pytest.raises(ValueError, match=r"k: shape \(600, 128\), expected \[rows, 4, 128\]"):
         hs2.v1_full_attn_select(b, q, k, k)
+
+
+def test_fp8_bridging_outputs_are_byte_caches():
+    h = torch.zeros(100, 256, dtype=torch.bfloat16)
+    w = [torch.zeros(256, 128, dtype=torch.bfloat16)]
+    with pytest.raises(TypeError, match="k_out: dtype torch.bfloat16"):
+        hs2.bridge_kv_fp8kv(h, w, w, 0.05, 0.05, k_out=[torch.zeros(100, 128, dtype=torch.bfloat16)],
+                            v_out=[torch.zeros(100, 128, dtype=torch.uint8)])
+    with pytest.raises(ValueError, match="one entry per layer"):
+        hs2.bridge_kv_fp8kv(h, w, w, [0.05, 0.05], 0.05)

@@ -642,6 +642,78 @@ def test_bridge_one_layer_and_tiny_rows():
     _bridge_check(bi, gk, gv, np.arange(37))
 
 
+def _bridge_fp8_check(bi, gk, gv, rows, k_sc, v_sc):
+    """GPU E4M3 codes against the oracle's encoding of the fp64 projection: a code may
+    differ only by one step, and only where the exact value lies within the GPU's
+    arithmetic error (fp32 accumulation as for the bf16 bridging, then one fp32 scaling)
+    of the midpoint between the two codes."""
+    H = stored_to_f64(bi.h[rows])
+    wk, wv = [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v]
+    ks, vs = oracle.bridge_kv(H, wk, wv)
+    kc, vc = oracle.bridge_kv_fp8(H, wk, wv, k_sc, v_sc)
+    idx = torch.as_tensor(rows, device=gk[0].device)
+    for l in range(len(wk)):
+        for got, val, codes, sc, what in ((gk[l], ks[l], kc[l], k_sc[l], "K"), (gv[l], vs[l], vc[l], v_sc[l], "V")):
+            g = got[idx].cpu().numpy()
+            assert g.dtype == np.uint8
+            mism = g != codes
+            if mism.any():
+                x = val[mism] / sc
+                dg, dr = oracle.e4m3_decode(g[mism]), oracle.e4m3_decode(codes[mism])
+                eps = np.abs(x) * 2.0 ** -21 + BRIDGE_ATOL / sc
+                mid = (dg + dr) / 2.0
+                # adjacent codes: no E4M3 value lies strictly between them, so the value
+                # nearest to their midpoint is one of the two
+                near = oracle.e4m3_decode(oracle.e4m3_encode(mid))
+                assert np.all((near == dg) | (near == dr)), f"{what}{l}: codes further apart than one step"
+                far = np.abs(x - mid) > eps
+                assert not far.any(), (f"{what}{l}: {far.sum()} codes differ away from a rounding midpoint, "
+                                       f"e.g. x={x[far][:3]}, gpu={dg[far][:3]}, oracle={dr[far][:3]}")
+            assert mism.mean() <= 1e-3, f"{what}{l}: {mism.mean():.2%} of the codes differ"
+
+
+def test_bridge_fp8_small_ragged_rows():
+    """3 layers (384-column tiles), 1,000 rows (a ragged last row tile), a different scale
+    for every tensor; with the smallest ones 5-14% of the values saturate."""
+    bi = make_bridge_inputs(1000, n_layers=3, seed=41)
+    k_sc, v_sc = [0.01, 0.02, 0.004], [0.012, 0.003, 0.03]
+    gk, gv = hs2.bridge_kv_fp8kv(to_dev(bi.h), [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v], k_sc, v_sc)
+    torch.cuda.synchronize()
+    assert bool((gk[2] == 0x7E).any()) and bool((gk[2] == 0xFE).any())   # saturated both ways
+    _bridge_fp8_check(bi, gk, gv, np.arange(1000), k_sc, v_sc)
+
+
+@pytest.mark.parametrize("n_layers", [1, 2, 6])
+def test_bridge_fp8_layer_counts(n_layers):
+    """The 256-column tiles (2L = 2 and 4 matrices) and four 384-column tiles (2L = 12),
+    each output matrix with its own scale."""
+    bi = make_bridge_inputs(600, n_layers=n_layers, seed=43 + n_layers, d_model=512 if n_layers == 1 else 2048)
+    k_sc = [0.008 + 0.001 * l for l in range(n_layers)]
+    v_sc = [0.011 - 0.001 * l for l in range(n_layers)]
+    gk, gv = hs2.bridge_kv_fp8kv(to_dev(bi.h), [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v], k_sc, v_sc)
+    _say(f"fp8 bridge {n_layers} layers")
+    _bridge_fp8_check(bi, gk, gv, np.arange(600), k_sc, v_sc)
+
+
+def test_bridge_fp8_then_fp8_selector():
+    """Bridged FP8 caches feed the FP8 selector and a sparse layer: the hidden states of
+    10,200 rows (three sequences) are projected into one layer's E4M3 K/V caches on the
+    GPU, and the selector and sparse layer on those caches match the oracle run on the
+    same codes."""
+    seqs = [3000, 5000, 2200]
+    spec = BlockSpec("bridged-fp8", seqs, [[2999, 1500], [4999, 300], [2199]], dtype="fp8", n_sparse=1,
+                     needles_per_query=0, seed=45, k_scale=0.01, v_scale=0.01)
+    inp = make_block_inputs(spec)
+    bi = make_bridge_inputs(sum(seqs), n_layers=1, seed=46)
+    gk, gv = hs2.bridge_kv_fp8kv(to_dev(bi.h), [to_dev(bi.w_k[0])], [to_dev(bi.w_v[0])], spec.k_scale, spec.v_scale)
+    torch.cuda.synchronize()
+    inp.k, inp.v = gk[0].cpu().numpy(), gv[0].cpu().numpy()
+    _bridge_fp8_check(bi, gk, gv, np.arange(0, sum(seqs), 7), [spec.k_scale], [spec.v_scale])
+    g = run_block(inp)
+    check_queries(inp, g, range(spec.total_q), "bridged-fp8")
+    check_all_queries_properties(inp, g)
+
+
 # ----------------------------------------------------------------------------------
 # the workloads at full size: sampled queries + properties of every query
 # ----------------------------------------------------------------------------------
@@ -686,6 +758,12 @@ def test_workload5_bridge_and_ragged_decode():
     rows = np.concatenate([np.arange(0, 300), np.random.default_rng(0).choice(1048576, 300, replace=False),
                            np.arange(1048576 - 300, 1048576)])
     _bridge_check(bi, gk, gv, rows)
+    del gk, gv
+    k_sc, v_sc = [0.01, 0.011, 0.012], [0.009, 0.01, 0.011]
+    _say("workload 5: FP8 bridging 1M x 2048 -> 3 layers")
+    gk, gv = hs2.bridge_kv_fp8kv(h, [to_dev(w) for w in bi.w_k], [to_dev(w) for w in bi.w_v], k_sc, v_sc)
+    torch.cuda.synchronize()
+    _bridge_fp8_check(bi, gk, gv, rows, k_sc, v_sc)
     del h, gk, gv
     torch.cuda.empty_cache()
     _full(5, range(32))

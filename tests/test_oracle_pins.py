@@ -359,6 +359,70 @@ def test_e4m3_decode_order_and_symmetry():
         assert np.all(blk == 2.0 ** (e - 10))
 
 
+# ----------------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache written by KV Bridging: the oracle's encoding
+# ----------------------------------------------------------------------------------
+
+def test_e4m3_encode_inverts_decode():
+    """Every finite code is the encoding of its own value (also -0.0 -> 0x80)."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(oracle.e4m3_encode(vals[fin]), codes[fin])
+
+
+def test_e4m3_encode_rounds_to_nearest_ties_to_even():
+    """Between the values of two adjacent finite codes, a value nearer to one takes that
+    code, and the midpoint itself the code with the even mantissa (low bit clear), across
+    the subnormals, the binade boundaries and both signs."""
+    d = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for base in (0x00, 0x80):
+        for c in range(base, base + 0x7E):
+            a, b = d[c], d[c + 1]           # codes c, c+1 (values decrease for negatives)
+            mid = (a + b) / 2.0
+            got = oracle.e4m3_encode(np.array([mid, mid + (a - mid) / 4, mid + (b - mid) / 4]))
+            even = c if c % 2 == 0 else c + 1
+            assert got.tolist() == [even, c, c + 1], (hex(c), a, b)
+
+
+def test_e4m3_encode_saturates_and_keeps_nan():
+    """Magnitudes above the largest finite value (448) give +-448, infinities too; NaN
+    gives 0x7F; values below half the smallest subnormal give a signed zero."""
+    x = np.array([448.0, 448.5, 464.0, 480.0, 1e30, np.inf, -449.0, -np.inf, np.nan, 2.0 ** -11, -2.0 ** -11])
+    assert oracle.e4m3_encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x00, 0x80]
+
+
+def test_e4m3_encode_matches_torch_float8():
+    """Random float32 values of every binade (including the subnormals), within +-464 where
+    torch's float8_e4m3fn conversion (a library routine) neither saturates nor gives NaN."""
+    rng = np.random.default_rng(5)
+    mag = np.exp2(rng.uniform(-12.0, np.log2(464.0), 200000)).astype(np.float32)
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_bridge_kv_fp8_error_bound():
+    """Each code of the FP8 bridging stands for the fp64 projection within half a step of
+    the E4M3 grid at that magnitude (relative 2^-4 for normals, 2^-10 absolute for the
+    subnormals), times the layer's scale; values beyond 448 * scale saturate."""
+    rng = np.random.default_rng(6)
+    H = rng.standard_normal((300, 64))
+    wk = [rng.standard_normal((64, 16)) * 0.02, rng.standard_normal((64, 16)) * 0.3]
+    wv = [rng.standard_normal((64, 16)) * 0.02, rng.standard_normal((64, 16)) * 0.3]
+    ks, vs = oracle.bridge_kv(H, wk, wv)
+    k_sc, v_sc = [0.004, 0.05], [0.003, 0.0001]     # the last one makes V_1 saturate
+    kc, vc = oracle.bridge_kv_fp8(H, wk, wv, k_sc, v_sc)
+    for ref, codes, sc in zip(ks + vs, kc + vc, k_sc + v_sc):
+        x = ref / sc
+        back = oracle.e4m3_decode(codes)
+        inside = np.abs(x) <= 448.0
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10)
+        assert np.all(np.abs(back - x)[inside] <= bound[inside])
+        assert np.all(np.abs(back[~inside]) == 448.0) and np.all(np.sign(back[~inside]) == np.sign(x[~inside]))
+    assert (np.abs(vs[1] / v_sc[1]) > 448.0).any()
+
+
 def test_fp8_block_inputs_round_trip():
     """The FP8 workload stores code(x / scale): decoding and rescaling returns x within
     half a step of the format (relative 2^-4 for normals), and planted needle keys
