@@ -260,6 +260,22 @@ hs2_status hs2_bridge_kv_append(const void* hidden, int32_t n_new, const int64_t
                                 void* workspace, size_t workspace_bytes, hs2_dtype dt,
                                 void* stream);
 
+/* The same append into FP8 E4M3 caches (the caches of hs2_bridge_kv_fp8kv and the *_fp8kv
+ * entry points): element c of the new row of layer l's K cache is the E4M3 code nearest
+ * to (h_i W_K^l)[c] / k_scale[l] (ties to the even mantissa, saturating at 448), computed
+ * as the fp32 sum times 1 / k_scale[l]; likewise for V.
+ *   k_cache, v_cache  HOST arrays of n_layers DEVICE pointers, each [cache_rows][head_dim]
+ *                     bytes of E4M3 codes, 16-byte aligned
+ *   k_scale, v_scale  HOST arrays of n_layers scales, each finite and > 0
+ *   Everything else as for hs2_bridge_kv_append (same workspace size).
+ */
+hs2_status hs2_bridge_kv_append_fp8kv(const void* hidden, int32_t n_new, const int64_t* rows,
+                                      int64_t cache_rows, int32_t d_model, int32_t n_layers,
+                                      const void* const* w_k, const void* const* w_v,
+                                      void* const* k_cache, void* const* v_cache,
+                                      const float* k_scale, const float* v_scale, int32_t head_dim,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * Exact causal attention of every query, without selection: the self-decoder's
  * full-attention layer in prefill ([arex] "Outer KV Bridging, inner KV Reuse": prefill

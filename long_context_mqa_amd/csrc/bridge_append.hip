@@ -73,9 +73,11 @@ __global__ __launch_bounds__(256) void append_partial_kernel(AppendArgs a) {
 }
 
 // Thread (new row, 8 consecutive output columns): the partials summed in slice order,
-// rounded to bf16 and written to the cache row of that token; rows outside
-// [0, cache_rows) are skipped.
-__global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a) {
+// rounded to bf16 (or, FP8 caches: scaled by the matrix's reciprocal scale, clamped to
+// +-448 and converted to E4M3 codes, round to nearest even) and written to the cache row
+// of that token; rows outside [0, cache_rows) are skipped.
+template <bool kFp8>
+__global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a, BridgeOut o) {
   const int cols = a.n_mats * kDim;
   const int per_row = cols / 8;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,21 +92,37 @@ __global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a) {
   }
   const int64_t row = a.rows[r];
   if (row < 0 || row >= a.cache_rows) return;
-  bf16x8 v;
+  if constexpr (kFp8) {
+    const float is = o.inv_scale[c / kDim];
+    float v[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = (__bf16)acc[q];
-  *reinterpret_cast<bf16x8*>(a.outs[c / kDim] + row * kDim + (c % kDim)) = v;
+    for (int q = 0; q < 8; ++q) v[q] = fminf(fmaxf(acc[q] * is, -448.0f), 448.0f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+    *reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(a.outs[c / kDim]) + row * kDim + (c % kDim)) =
+        make_int2(w0, w1);
+  } else {
+    bf16x8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (__bf16)acc[q];
+    *reinterpret_cast<bf16x8*>(a.outs[c / kDim] + row * kDim + (c % kDim)) = v;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_bridge_append(const AppendArgs& a, hipStream_t s) {
+hipError_t launch_bridge_append(const AppendArgs& a, const BridgeOut& o, hipStream_t s) {
   const dim3 grid(a.n_slices, a.n_mats, (a.n_new + kTile - 1) / kTile);
   hipLaunchKernelGGL(append_partial_kernel, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int threads = a.n_new * (a.n_mats * kDim / 8);
-  hipLaunchKernelGGL(append_finish_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, a);
+  if (o.fp8)
+    hipLaunchKernelGGL(append_finish_kernel<true>, dim3((threads + 255) / 256), dim3(256), 0, s, a, o);
+  else
+    hipLaunchKernelGGL(append_finish_kernel<false>, dim3((threads + 255) / 256), dim3(256), 0, s, a, o);
   return hipGetLastError();
 }
 

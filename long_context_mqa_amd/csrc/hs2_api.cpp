@@ -705,6 +705,66 @@ hs2_status causal_impl(const hs2_seqs* batch, const void* q, const void* k, cons
   return ok();
 }
 
+// Both append entry points: bf16 cache rows, or (k_scale and v_scale given) FP8 E4M3 codes.
+hs2_status append_impl(const void* hidden, int32_t n_new, const int64_t* rows, int64_t cache_rows, int32_t d_model,
+                       int32_t n_layers, const void* const* w_k, const void* const* w_v, void* const* k_cache,
+                       void* const* v_cache, const float* k_scale, const float* v_scale, int32_t head_dim,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "bridging supports head_dim=128 only (got %d)", head_dim);
+  if (d_model < kAppendSlice || d_model > 65536 || d_model % kAppendSlice != 0)
+    return fail(HS2_ERR_UNSUPPORTED, "d_model must be a multiple of %d in [%d, 65536] (got %d)", kAppendSlice,
+                kAppendSlice, d_model);
+  if (n_layers < 1 || n_layers > 8) return fail(HS2_ERR_UNSUPPORTED, "n_layers must be in [1, 8] (got %d)", n_layers);
+  if (n_new < 0 || n_new > 65536) return fail(HS2_ERR_INVALID_ARG, "n_new must be in [0, 65536] (got %d)", n_new);
+  if (cache_rows < 0) return fail(HS2_ERR_INVALID_ARG, "cache_rows must be >= 0");
+  if (!w_k || !w_v || !k_cache || !v_cache) return fail(HS2_ERR_INVALID_ARG, "pointer arrays must not be NULL");
+  if (n_new > 0 && (!hidden || !rows)) return fail(HS2_ERR_INVALID_ARG, "hidden and rows must not be NULL");
+  if (!aligned(hidden, 16) || !aligned(rows, 8)) return fail(HS2_ERR_INVALID_ARG, "hidden must be 16-byte and rows 8-byte aligned");
+  AppendArgs a{};
+  BridgeOut o{};
+  o.fp8 = k_scale != nullptr ? 1 : 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!w_k[l] || !w_v[l] || !k_cache[l] || !v_cache[l])
+      return fail(HS2_ERR_INVALID_ARG, "a weight or cache pointer of layer %d is NULL", l);
+    if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
+      return fail(HS2_ERR_INVALID_ARG, "weights and caches must be 16-byte aligned (layer %d)", l);
+    if (o.fp8) {
+      const float ks = k_scale[l], vs = v_scale[l];
+      if (!(std::isfinite(ks) && ks > 0.0f && std::isfinite(vs) && vs > 0.0f))
+        return fail(HS2_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0 (layer %d)", l);
+      const float ik = 1.0f / ks, iv = 1.0f / vs;
+      if (!std::isfinite(ik) || !std::isfinite(iv))
+        return fail(HS2_ERR_INVALID_ARG, "the reciprocal of a scale overflows (layer %d)", l);
+      o.inv_scale[2 * l] = ik;
+      o.inv_scale[2 * l + 1] = iv;
+    }
+    a.w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    a.w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    a.outs[2 * l] = static_cast<uint16_t*>(k_cache[l]);
+    a.outs[2 * l + 1] = static_cast<uint16_t*>(v_cache[l]);
+  }
+  const size_t need = hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, head_dim);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes, need);
+  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (n_new == 0) return ok();
+  a.h = static_cast<const uint16_t*>(hidden);
+  a.rows = rows;
+  a.part = static_cast<float*>(workspace);
+  a.cache_rows = cache_rows;
+  a.n_new = n_new;
+  a.d_model = d_model;
+  a.n_mats = 2 * n_layers;
+  a.n_slices = d_model / kAppendSlice;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LaunchMarks mk(s);
+  hipError_t e = mk.before(0);
+  if (e == hipSuccess) e = launch_bridge_append(a, o, s);
+  if (e == hipSuccess) e = mk.after(0);
+  if (e != hipSuccess) return hip_fail(e, "bridging append launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -782,47 +842,18 @@ hs2_status hs2_bridge_kv_append(const void* hidden, int32_t n_new, const int64_t
                                 void* const* k_cache, void* const* v_cache, int32_t head_dim, void* workspace,
                                 size_t workspace_bytes, hs2_dtype dt, void* stream) {
   if (dt != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "bridging supports bf16 only");
-  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "bridging supports head_dim=128 only (got %d)", head_dim);
-  if (d_model < kAppendSlice || d_model > 65536 || d_model % kAppendSlice != 0)
-    return fail(HS2_ERR_UNSUPPORTED, "d_model must be a multiple of %d in [%d, 65536] (got %d)", kAppendSlice,
-                kAppendSlice, d_model);
-  if (n_layers < 1 || n_layers > 8) return fail(HS2_ERR_UNSUPPORTED, "n_layers must be in [1, 8] (got %d)", n_layers);
-  if (n_new < 0 || n_new > 65536) return fail(HS2_ERR_INVALID_ARG, "n_new must be in [0, 65536] (got %d)", n_new);
-  if (cache_rows < 0) return fail(HS2_ERR_INVALID_ARG, "cache_rows must be >= 0");
-  if (!w_k || !w_v || !k_cache || !v_cache) return fail(HS2_ERR_INVALID_ARG, "pointer arrays must not be NULL");
-  if (n_new > 0 && (!hidden || !rows)) return fail(HS2_ERR_INVALID_ARG, "hidden and rows must not be NULL");
-  if (!aligned(hidden, 16) || !aligned(rows, 8)) return fail(HS2_ERR_INVALID_ARG, "hidden must be 16-byte and rows 8-byte aligned");
-  AppendArgs a{};
-  for (int l = 0; l < n_layers; ++l) {
-    if (!w_k[l] || !w_v[l] || !k_cache[l] || !v_cache[l])
-      return fail(HS2_ERR_INVALID_ARG, "a weight or cache pointer of layer %d is NULL", l);
-    if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_cache[l], 16) || !aligned(v_cache[l], 16))
-      return fail(HS2_ERR_INVALID_ARG, "weights and caches must be 16-byte aligned (layer %d)", l);
-    a.w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
-    a.w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
-    a.outs[2 * l] = static_cast<uint16_t*>(k_cache[l]);
-    a.outs[2 * l + 1] = static_cast<uint16_t*>(v_cache[l]);
-  }
-  const size_t need = hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, head_dim);
-  if (workspace_bytes < need || (need > 0 && !workspace))
-    return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the required %zu", workspace_bytes, need);
-  if (workspace && !aligned(workspace, kAlign)) return fail(HS2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (n_new == 0) return ok();
-  a.h = static_cast<const uint16_t*>(hidden);
-  a.rows = rows;
-  a.part = static_cast<float*>(workspace);
-  a.cache_rows = cache_rows;
-  a.n_new = n_new;
-  a.d_model = d_model;
-  a.n_mats = 2 * n_layers;
-  a.n_slices = d_model / kAppendSlice;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  LaunchMarks mk(s);
-  hipError_t e = mk.before(0);
-  if (e == hipSuccess) e = launch_bridge_append(a, s);
-  if (e == hipSuccess) e = mk.after(0);
-  if (e != hipSuccess) return hip_fail(e, "bridging append launch");
-  return ok();
+  return append_impl(hidden, n_new, rows, cache_rows, d_model, n_layers, w_k, w_v, k_cache, v_cache, nullptr,
+                     nullptr, head_dim, workspace, workspace_bytes, stream);
+}
+
+hs2_status hs2_bridge_kv_append_fp8kv(const void* hidden, int32_t n_new, const int64_t* rows, int64_t cache_rows,
+                                      int32_t d_model, int32_t n_layers, const void* const* w_k,
+                                      const void* const* w_v, void* const* k_cache, void* const* v_cache,
+                                      const float* k_scale, const float* v_scale, int32_t head_dim, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!k_scale || !v_scale) return fail(HS2_ERR_INVALID_ARG, "k_scale and v_scale must not be NULL");
+  return append_impl(hidden, n_new, rows, cache_rows, d_model, n_layers, w_k, w_v, k_cache, v_cache, k_scale,
+                     v_scale, head_dim, workspace, workspace_bytes, stream);
 }
 
 size_t hs2_bridge_kv_workspace_size(int32_t d_model, int32_t n_layers, int32_t head_dim) {

@@ -49,7 +49,7 @@ struct BridgeOut {
   float inv_scale[16];
 };
 hipError_t launch_bridge_gemm(const BridgeArgs& a, const BridgeOut& o, hipStream_t s);
-hipError_t launch_bridge_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_bridge_append(const AppendArgs& a, const BridgeOut& o, hipStream_t s);
 
 hipError_t launch_v1_attn(const V1AttnArgs& a, bool sparse, int grid, hipStream_t s);
 hipError_t launch_v1_select(const V1SelectArgs& a, hipStream_t s);

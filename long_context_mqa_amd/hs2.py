@@ -35,6 +35,7 @@ EXPORTED = [
     "hs2_sparse_attn_noalloc",
     "hs2_bridge_kv_append_workspace_size",
     "hs2_bridge_kv_append",
+    "hs2_bridge_kv_append_fp8kv",
     "hs2_causal_attn_workspace_size",
     "hs2_causal_attn",
     "hs2_full_attn_select_fp8kv",
@@ -105,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs2_bridge_kv_append_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hs2_bridge_kv_append.restype = I32
     lib.hs2_bridge_kv_append.argtypes = [P, I32, P, I64, I32, I32, P, P, P, P, I32, P, SZ, I32, P]
+    lib.hs2_bridge_kv_append_fp8kv.restype = I32
+    lib.hs2_bridge_kv_append_fp8kv.argtypes = [P, I32, P, I64, I32, I32, P, P, P, P, P, P, I32, P, SZ, P]
     lib.hs2_causal_attn_workspace_size.restype = SZ
     lib.hs2_causal_attn_workspace_size.argtypes = [SP, I32, I32, I32]
     lib.hs2_causal_attn.restype = I32
@@ -524,6 +527,41 @@ def bridge_kv_append(h, rows, w_k, w_v, k_cache, v_cache, workspace=None, stream
                                     arr(*[w.data_ptr() for w in w_k]), arr(*[w.data_ptr() for w in w_v]),
                                     arr(*[c.data_ptr() for c in k_cache]), arr(*[c.data_ptr() for c in v_cache]),
                                     128, _ptr(workspace), workspace.numel(), HS2_BF16, _stream(stream)))
+
+
+def bridge_kv_append_fp8kv(h, rows, w_k, w_v, k_cache, v_cache, k_scale, v_scale, workspace=None, stream=None):
+    """hs2_bridge_kv_append_fp8kv: the new tokens' K/V rows written as E4M3 codes into FP8
+    caches (uint8 [cache_rows, 128]); k_scale and v_scale are one float for every layer or
+    a list with one per layer."""
+    lib = load()
+    n_layers = len(w_k)
+    n_new, d_model = int(h.shape[0]), int(h.shape[1])
+    assert rows.dtype == torch.int64 and rows.numel() == n_new
+    ks = [float(k_scale)] * n_layers if isinstance(k_scale, (int, float)) else [float(x) for x in k_scale]
+    vs = [float(v_scale)] * n_layers if isinstance(v_scale, (int, float)) else [float(x) for x in v_scale]
+    if len(w_v) != n_layers or len(k_cache) != n_layers or len(v_cache) != n_layers or len(ks) != n_layers or \
+            len(vs) != n_layers:
+        raise ValueError("w_k, w_v, k_cache, v_cache and the scales must hold one entry per layer")
+    cache_rows = int(k_cache[0].shape[0])
+    _expect("h", h, (torch.bfloat16,), (d_model,), n_new)
+    for name, ts in (("w_k", w_k), ("w_v", w_v)):
+        for t in ts:
+            _expect(name, t, (torch.bfloat16,), (128,), d_model, h.device)
+    for name, ts in (("k_cache", k_cache), ("v_cache", v_cache)):
+        for t in ts:
+            _expect(name, t, (torch.uint8, torch.float8_e4m3fn), (128,), cache_rows, h.device)
+            if int(t.shape[0]) != cache_rows:
+                raise ValueError("every cache must have the same number of rows")
+    arr = ctypes.c_void_p * n_layers
+    farr = ctypes.c_float * n_layers
+    need = lib.hs2_bridge_kv_append_workspace_size(n_new, d_model, n_layers, 128)
+    if workspace is None:
+        workspace = _workspace(need, h.device)
+    _check(lib.hs2_bridge_kv_append_fp8kv(_ptr(h), n_new, _ptr(rows), cache_rows, d_model, n_layers,
+                                          arr(*[w.data_ptr() for w in w_k]), arr(*[w.data_ptr() for w in w_v]),
+                                          arr(*[c.data_ptr() for c in k_cache]), arr(*[c.data_ptr() for c in v_cache]),
+                                          farr(*ks), farr(*vs), 128, _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------

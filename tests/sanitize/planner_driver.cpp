@@ -211,7 +211,7 @@ hipError_t launch_bridge_gemm(const BridgeArgs& a, const BridgeOut&, hipStream_t
   in_ws(a.wt, (size_t)a.n_mats * kDim * a.d_model * 2);
   return hipSuccess;
 }
-hipError_t launch_bridge_append(const AppendArgs& a, hipStream_t) {
+hipError_t launch_bridge_append(const AppendArgs& a, const BridgeOut&, hipStream_t) {
   ++g_launches;
   CHECK(a.n_slices * kAppendSlice == a.d_model);
   in_ws(a.part, (size_t)a.n_slices * a.n_new * a.n_mats * kDim * 4);

@@ -152,6 +152,26 @@ def test_fp8_bridge_rejects_bad_arguments(lib):
     assert call(ws_bytes=ws - 2) == hs2.HS2_ERR_WORKSPACE
 
 
+def test_fp8_append_rejects_bad_arguments(lib):
+    """The FP8 append checks everything hs2_bridge_kv_append checks, plus its scales."""
+    P = ctypes.c_void_p * 2
+    F = ctypes.c_float * 2
+    w = P(FAKE, FAKE)
+    c = P(FAKE * 2, FAKE * 3)
+    ws = lib.hs2_bridge_kv_append_workspace_size(64, 2048, 2, 128)
+    good = F(0.05, 0.05)
+
+    def call(ks=good, vs=good, n_new=64, ws_bytes=ws, hd=128):
+        return lib.hs2_bridge_kv_append_fp8kv(FAKE * 5, n_new, FAKE * 6, 3000, 2048, 2, w, w, c, c, ks, vs, hd,
+                                              FAKE * 8, ws_bytes, None)
+    assert call(ks=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(vs=F(0.05, 0.0)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(ks=F(float("inf"), 0.05)) == hs2.HS2_ERR_INVALID_ARG
+    assert call(n_new=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(hd=64) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(ws_bytes=ws - 1) == hs2.HS2_ERR_WORKSPACE
+
+
 def test_workspace_sizes_grow_with_the_batch(lib):
     small = _batch(total_q=4, max_kv_len=8192, rows=8192 * 4, num_seqs=4)
     big = _batch(total_q=64, max_kv_len=131072, rows=131072 * 64, num_seqs=64)

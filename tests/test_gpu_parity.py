@@ -523,6 +523,68 @@ def test_bridge_append_then_select():
     check_queries(inp, g, range(spec.total_q), "append-step")
 
 
+@pytest.mark.parametrize("n_new,d_model", [(37, 2048), (64, 256), (1, 128)])
+def test_bridge_append_fp8_rows(n_new, d_model):
+    """The FP8 append: new tokens' E4M3 codes into 3 layers' FP8 caches at scattered rows
+    (two out of range, skipped), a scale per tensor; every other byte of the caches is kept."""
+    bi = make_bridge_inputs(n_new, n_layers=3, seed=38 + n_new, d_model=d_model)
+    cache_rows = 3000
+    rows = np.random.default_rng(n_new + 1).choice(cache_rows, n_new, replace=False).astype(np.int64)
+    if n_new > 8:
+        rows[5], rows[6] = cache_rows + 10, -1
+    init = [np.random.default_rng(100 + i).integers(0, 256, (cache_rows, 128), dtype=np.uint8) for i in range(6)]
+    caches = [torch.from_numpy(c).cuda() for c in init]
+    k_sc, v_sc = [0.004, 0.01, 0.02], [0.02, 0.003, 0.01]
+    hs2.bridge_kv_append_fp8kv(to_dev(bi.h), torch.from_numpy(rows).cuda(), [to_dev(w) for w in bi.w_k],
+                               [to_dev(w) for w in bi.w_v], caches[0::2], caches[1::2], k_sc, v_sc)
+    torch.cuda.synchronize()
+    valid = (rows >= 0) & (rows < cache_rows)
+    H = stored_to_f64(bi.h)
+    wk, wv = [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v]
+    ks, vs = oracle.bridge_kv(H, wk, wv)
+    kc, vc = oracle.bridge_kv_fp8(H, wk, wv, k_sc, v_sc)
+    keep = np.ones(cache_rows, bool)
+    keep[rows[valid]] = False
+    for l in range(3):
+        for c0, c, val, codes, sc, what in ((init[2 * l], caches[2 * l], ks[l], kc[l], k_sc[l], f"K{l}"),
+                                            (init[2 * l + 1], caches[2 * l + 1], vs[l], vc[l], v_sc[l], f"V{l}")):
+            got = c.cpu().numpy()
+            assert np.array_equal(got[keep], c0[keep]), f"{what}: a row not appended changed"
+            _check_fp8_codes(got[rows[valid]], val[valid], codes[valid], sc, what)
+
+
+def test_bridge_append_fp8_then_select():
+    """One decode step on FP8 caches: the FP8 append writes each sequence's current-token
+    row of layer 0, then the FP8 selector and a sparse layer read the caches and match the
+    oracle run on the same codes."""
+    spec = BlockSpec("append-step-fp8", [3000, 5000, 2200], [[2999], [4999], [2199]], dtype="fp8", n_sparse=1,
+                     needles_per_query=2, seed=47)
+    inp = make_block_inputs(spec)
+    bi = make_bridge_inputs(3, n_layers=1, seed=48)
+    rows = (inp.kv_start + inp.kv_len - 1).astype(np.int64)
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    hs2.bridge_kv_append_fp8kv(to_dev(bi.h), torch.from_numpy(rows).cuda(), [to_dev(bi.w_k[0])],
+                               [to_dev(bi.w_v[0])], [k], [v], spec.k_scale, spec.v_scale)
+    torch.cuda.synchronize()
+    H = stored_to_f64(bi.h)
+    ks, vs = oracle.bridge_kv(H, [stored_to_f64(bi.w_k[0])], [stored_to_f64(bi.w_v[0])])
+    kc, vc = oracle.bridge_kv_fp8(H, [stored_to_f64(bi.w_k[0])], [stored_to_f64(bi.w_v[0])], [spec.k_scale],
+                                  [spec.v_scale])
+    gk, gv = k.cpu().numpy(), v.cpu().numpy()
+    _check_fp8_codes(gk[rows], ks[0], kc[0], spec.k_scale, "K0")
+    _check_fp8_codes(gv[rows], vs[0], vc[0], spec.v_scale, "V0")
+    inp.k[rows], inp.v[rows] = gk[rows], gv[rows]
+    batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, "cuda")
+    out, lse, sel, cnt = hs2.full_attn_select_fp8kv(batch, to_dev(inp.q_sel), k, v, spec.k_scale, spec.v_scale,
+                                                    spec.window, spec.top_k, spec.scale)
+    o1, _ = hs2.sparse_attn_fp8kv(batch, to_dev(inp.q_sp[0]), k, v, spec.k_scale, spec.v_scale, sel, spec.window,
+                                  spec.top_k, spec.scale)
+    torch.cuda.synchronize()
+    g = {"out": from_dev(out), "lse": from_dev(lse), "sel": sel.cpu().numpy(), "count": cnt.cpu().numpy(),
+         "sparse": [from_dev(o1)]}
+    check_queries(inp, g, range(spec.total_q), "append-step-fp8")
+
+
 # ----------------------------------------------------------------------------------
 # exact causal attention without selection (prefill of the self-decoder's full layer)
 # ----------------------------------------------------------------------------------
@@ -642,34 +704,38 @@ def test_bridge_one_layer_and_tiny_rows():
     _bridge_check(bi, gk, gv, np.arange(37))
 
 
+def _check_fp8_codes(g, val, codes, sc, what):
+    """GPU E4M3 codes g against the oracle's codes of val / sc: a code may differ only by
+    one step, and only where the exact value lies within the GPU's arithmetic error (fp32
+    accumulation as for the bf16 bridging, then one fp32 scaling) of the midpoint between
+    the two codes."""
+    assert g.dtype == np.uint8
+    mism = g != codes
+    if mism.any():
+        x = val[mism] / sc
+        dg, dr = oracle.e4m3_decode(g[mism]), oracle.e4m3_decode(codes[mism])
+        eps = np.abs(x) * 2.0 ** -21 + BRIDGE_ATOL / sc
+        mid = (dg + dr) / 2.0
+        # adjacent codes: no E4M3 value lies strictly between them, so the value
+        # nearest to their midpoint is one of the two
+        near = oracle.e4m3_decode(oracle.e4m3_encode(mid))
+        assert np.all((near == dg) | (near == dr)), f"{what}: codes further apart than one step"
+        far = np.abs(x - mid) > eps
+        assert not far.any(), (f"{what}: {far.sum()} codes differ away from a rounding midpoint, "
+                               f"e.g. x={x[far][:3]}, gpu={dg[far][:3]}, oracle={dr[far][:3]}")
+    assert mism.mean() <= 1e-3, f"{what}: {mism.mean():.2%} of the codes differ"
+
+
 def _bridge_fp8_check(bi, gk, gv, rows, k_sc, v_sc):
-    """GPU E4M3 codes against the oracle's encoding of the fp64 projection: a code may
-    differ only by one step, and only where the exact value lies within the GPU's
-    arithmetic error (fp32 accumulation as for the bf16 bridging, then one fp32 scaling)
-    of the midpoint between the two codes."""
+    """The FP8 bridging of the given rows against the oracle's (bridge_kv_fp8)."""
     H = stored_to_f64(bi.h[rows])
     wk, wv = [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v]
     ks, vs = oracle.bridge_kv(H, wk, wv)
     kc, vc = oracle.bridge_kv_fp8(H, wk, wv, k_sc, v_sc)
     idx = torch.as_tensor(rows, device=gk[0].device)
     for l in range(len(wk)):
-        for got, val, codes, sc, what in ((gk[l], ks[l], kc[l], k_sc[l], "K"), (gv[l], vs[l], vc[l], v_sc[l], "V")):
-            g = got[idx].cpu().numpy()
-            assert g.dtype == np.uint8
-            mism = g != codes
-            if mism.any():
-                x = val[mism] / sc
-                dg, dr = oracle.e4m3_decode(g[mism]), oracle.e4m3_decode(codes[mism])
-                eps = np.abs(x) * 2.0 ** -21 + BRIDGE_ATOL / sc
-                mid = (dg + dr) / 2.0
-                # adjacent codes: no E4M3 value lies strictly between them, so the value
-                # nearest to their midpoint is one of the two
-                near = oracle.e4m3_decode(oracle.e4m3_encode(mid))
-                assert np.all((near == dg) | (near == dr)), f"{what}{l}: codes further apart than one step"
-                far = np.abs(x - mid) > eps
-                assert not far.any(), (f"{what}{l}: {far.sum()} codes differ away from a rounding midpoint, "
-                                       f"e.g. x={x[far][:3]}, gpu={dg[far][:3]}, oracle={dr[far][:3]}")
-            assert mism.mean() <= 1e-3, f"{what}{l}: {mism.mean():.2%} of the codes differ"
+        _check_fp8_codes(gk[l][idx].cpu().numpy(), ks[l], kc[l], k_sc[l], f"K{l}")
+        _check_fp8_codes(gv[l][idx].cpu().numpy(), vs[l], vc[l], v_sc[l], f"V{l}")
 
 
 def test_bridge_fp8_small_ragged_rows():
