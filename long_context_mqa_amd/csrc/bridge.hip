@@ -25,7 +25,10 @@
 // The results leave through LDS: a store straight from the MFMA layout writes 32 rows x 16
 // bytes per instruction, and those stores cost about 10% of the kernel; written as bf16 rows
 // into the (then idle) stage area and read back, each store instruction covers four whole
-// 256-byte rows (5% faster overall). Measured and not kept: four waves (one per SIMD) on
+// 256-byte rows (5% faster overall). For an FP8 KV cache ([arex] "Numbers computed on three
+// 80B-A3B models" accounts the cache in FP8) the same epilogue writes OCP E4M3 codes instead:
+// each value times its output matrix's reciprocal scale, clamped to +-448, converted with
+// round to nearest even; a store then covers eight 128-byte rows (no slower than bf16). Measured and not kept: four waves (one per SIMD) on
 // 256 x 256 tiles with AGPR accumulators and double-buffered operand registers (2% slower);
 // a persistent grid carrying the copy stream across tiles (8% slower); touching the lines of
 // stage k+3 ahead of their copies (4% slower: the copies were not waiting on HBM).
