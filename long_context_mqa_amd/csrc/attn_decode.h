@@ -134,8 +134,7 @@ __global__ __launch_bounds__(64 * kW) void attn_bf16_kernel(AttnArgs a, WorkList
   const bool valid = __builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t));
   // the descriptor is the same on every lane (query i): keep the loop control scalar
   t = __builtin_amdgcn_readfirstlane(t);
-  base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
-                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
+  base = (int64_t)uniform_u64((uint64_t)base);
   if (a.n_split == 1 && hist != nullptr) {
     for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) hist[(size_t)i * kHistBins + e] = 0u;
     if (threadIdx.x < 4) counters[(size_t)i * 4 + threadIdx.x] = 0u;

@@ -69,8 +69,7 @@ __device__ inline bool v1_query(const SeqsDev& b, int i, int& s, int64_t& base, 
 }
 
 __device__ inline int64_t uniform64(int64_t x) {
-  return (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32)) << 32) |
-                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)x));
+  return (int64_t)uniform_u64((uint64_t)x);
 }
 
 // Where the keys of one wave's tile list live. Tile `it` holds 32 keys; key kk of it is

@@ -67,6 +67,15 @@ __device__ inline bool query_desc(const SeqsDev& b, int i, int64_t& base, int& t
   return ok;
 }
 
+// A wave-uniform 64-bit value moved to scalar registers, half by half. readfirstlane
+// returns a signed int, so each half goes back through uint32_t before it is widened: a low
+// half with bit 31 set would otherwise sign-extend over the high half.
+__device__ inline uint64_t uniform_u64(uint64_t x) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
 // One wave-wide 16-byte-per-lane copy from global memory straight into LDS: lane l's
 // 16 bytes land at LDS byte address `lds` + 16*l (`lds` must be wave-uniform). Issued as
 // asm so that the wait for it can be placed by hand with s_waitcnt vmcnt (the compiler

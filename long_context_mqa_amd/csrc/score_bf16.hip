@@ -91,8 +91,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
   const bool valid = __builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t));
   // the descriptor is the same on every lane (query i): keep the loop control scalar
   t = __builtin_amdgcn_readfirstlane(t);
-  base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
-                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
+  base = (int64_t)uniform_u64((uint64_t)base);
   const int nc = max(0, t - a.window + 1);
   const int k0 = split * a.split_keys;
   if (wl.n > 0 && a.plan_miss != nullptr && threadIdx.x == 0 && last_planned(wl, i))

@@ -296,8 +296,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void sparse_attn_kernel(AttnArgs a) 
   int t;
   const bool valid = __builtin_amdgcn_readfirstlane(query_desc(a.b, i, base, t));
   t = __builtin_amdgcn_readfirstlane(t);
-  base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)base >> 32)) << 32) |
-                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
+  base = (int64_t)uniform_u64((uint64_t)base);
   // the copies below are waited for by hand: every compiler-tracked load (Q included) must
   // have completed before the first one is issued
 #pragma unroll
