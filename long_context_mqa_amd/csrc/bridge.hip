@@ -15,8 +15,8 @@
 // C^T = W^T H^T with eight waves, two per SIMD, of 128 rows x 96 columns (64 x 128 for the
 // 256-column tile). The wider tile re-reads each H row 2L/3 times instead of L times; the
 // 128 x 96 wave tile reads 7 operand fragments from LDS per 12 MFMAs (8 for 64 x 192, which
-// measured 1.5-2% slower), and its 192 accumulator registers per lane still allow two
-// waves per SIMD. Operand tiles stream through two LDS stages 64 deep in the contraction
+// measured 1.5-2% slower), and its 192 fp32 accumulators per lane still allow two
+// waves per SIMD (251 registers in all). Operand tiles stream through two LDS stages 64 deep in the contraction
 // (80 KB each) by direct-to-LDS loads: one barrier per 64 of depth (half as many as with
 // 32-deep stages, which measured 15% slower on random data even with a third stage).
 // Tiles of the same rows run back to back on one XCD, so H is read from HBM once and

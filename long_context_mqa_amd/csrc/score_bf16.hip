@@ -5,8 +5,10 @@
 // publishes the MiMo-V3 core architecture HySparse2", section "Outer KV Bridging, inner
 // KV Reuse": the full-attention layer's scores select the keys the sparse layers attend.
 //
-// Built with the MFMA results in VGPRs (no accumulator registers): the loop needs about
-// 180 registers, and the softmax reads every result element once per tile.
+// Built with the MFMA results in VGPRs (MFMA destinations are not accumulator registers):
+// the exponentials read every result element once per tile. The bf16 build (one wave per
+// SIMD) takes 256 VGPRs and keeps other values in 64 accumulator registers; the FP8 build
+// (two waves per SIMD) fits in 256 VGPRs.
 #include "attn_common.h"
 #include "hs2_launch.h"
 
@@ -31,7 +33,7 @@ constexpr int kSBufTiles = 128;  // tiles of scores staged per workgroup before 
 
 // Waves per workgroup: 4 for bf16 tiles (one per SIMD; the pass is bound by HBM) and 8 for
 // FP8 tiles (two per SIMD), whose tiles arrive twice as fast per byte and would otherwise
-// leave one wave's MFMA, conversion and exp chain exposed; 186 registers per lane fit
+// leave one wave's MFMA, conversion and exp chain exposed; its 256 registers per lane fit
 // two waves per SIMD.
 template <typename Kv>
 struct ScoreCfg {
