@@ -89,6 +89,12 @@ def test_p1_brute_force(H, d, n, t, W, k, seed):
     if chosen and len(chosen) < len(cands):
         unchosen = [j for j in cands if j not in chosen]
         assert min(float(score[j]) for j in chosen) >= max(float(score[j]) for j in unchosen)
+    # tau, the k-th largest candidate score (the parity band is built on it): the smallest
+    # score of the brute-force choice; none when every candidate (or none) is taken
+    if 0 < k < len(cands):
+        assert r["tau"] == pytest.approx(min(float(score[j]) for j in chosen), rel=1e-12, abs=0)
+    else:
+        assert r["tau"] is None
 
 
 # ----------------------------------------------------------------------------------
