@@ -99,6 +99,12 @@ def test_v1_brute_force(t, top_blocks, window, seed):
     np.testing.assert_allclose(r["scores"], np.array(score), rtol=1e-12, atol=1e-15)
     for g in range(G):
         assert r["sel"][g].tolist() == chosen[g]
+        # tau (the block parity band is built on it): the smallest score of the brute-force
+        # choice of rank top_blocks; none when every candidate block is kept
+        if top_blocks < len(score[g]):
+            assert r["tau"][g] == pytest.approx(float(min(score[g][b] for b in chosen[g])), rel=1e-12, abs=0)
+        else:
+            assert r["tau"][g] is None
     o, _, _ = v1.v1_sparse_query(q, K, V, t, r["sel"], Ks, Vs, gsp, gsw, scale, window)
     np.testing.assert_allclose(o, out, rtol=1e-11, atol=1e-13)
 
