@@ -18,6 +18,13 @@ Comparison rules:
     64 x 128 values and a max of up to 1.02e-2 (an element of magnitude 4.3, where half a
     bf16 unit is 1.6e-2), so the plain rules would reject the exact result.
   * LSE: |gpu - fp64| <= 1e-3 (fp32 output of a value of magnitude ~10).
+  * bridging, bf16 outputs: |gpu - fp64| <= 1 bf16 ulp + 2^-14 everywhere (the absolute
+    part covers an fp32 accumulation of d_model products near zero), at most 1% of the
+    values differing from the correctly rounded reference, and a mean distance to it of at
+    most 1e-4.
+  * bridging, FP8 E4M3 outputs: a code may differ from the oracle's code of value/scale
+    only by one step, only where the value lies within the GPU's arithmetic error of the
+    midpoint between the two codes, and at most 0.1% of the codes may differ.
 """
 from __future__ import annotations
 
@@ -25,13 +32,14 @@ import numpy as np
 import torch
 
 import oracle
-from workloads.gen import stored_to_f64
+from workloads.gen import bf16_round, bf16_to_f32, stored_to_f64
 
 REL_BAND = 1e-5
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 LSE_ABS = 1e-3
 FEW_KEYS = 4      # attended keys up to which the mean is taken beyond output rounding
+BRIDGE_ATOL = 2.0 ** -14  # fp32 accumulation of d_model products, for outputs near zero
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -89,6 +97,47 @@ def check_attn(gpu: np.ndarray, ref: np.ndarray, what: str = "", beyond_rounding
 def check_lse(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
     err = np.abs(gpu - ref)
     assert err.max() <= LSE_ABS, f"{what}: lse max abs err {err.max():.3e}"
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """One bfloat16 unit in the last place at |x|."""
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 7)
+
+
+def check_bridge_bf16(g: np.ndarray, ref: np.ndarray, what: str = ""):
+    """bf16 bridging outputs g (widened) against the fp64 projection ref."""
+    err = np.abs(g - ref)
+    bad = err > bf16_ulp(ref) + BRIDGE_ATOL
+    assert not bad.any(), (f"{what}: {bad.sum()} values beyond tolerance, worst err "
+                           f"{err[bad].max():.3e} at |ref| {np.abs(ref[bad]).min():.3e}")
+    # against the correctly rounded bf16 value: bf16 output quantisation alone gives a mean
+    # |error| of ~1e-3 against fp64 for outputs of this size
+    ref_b = bf16_to_f32(bf16_round(ref.astype(np.float32))).astype(np.float64)
+    mism = g != ref_b
+    assert mism.mean() <= 1e-2, f"{what}: {mism.mean():.2%} differ from the rounded reference"
+    assert np.abs(g - ref_b).mean() <= 1e-4, f"{what}: mean distance to the rounded reference"
+
+
+def check_fp8_codes(g: np.ndarray, val: np.ndarray, codes: np.ndarray, sc: float, what: str = ""):
+    """GPU E4M3 codes g against the oracle's codes of val / sc: a code may differ only by
+    one step, and only where the exact value lies within the GPU's arithmetic error (fp32
+    accumulation as for the bf16 bridging, then one fp32 scaling) of the midpoint between
+    the two codes."""
+    assert g.dtype == np.uint8
+    mism = g != codes
+    if mism.any():
+        x = val[mism] / sc
+        dg, dr = oracle.e4m3_decode(g[mism]), oracle.e4m3_decode(codes[mism])
+        eps = np.abs(x) * 2.0 ** -21 + BRIDGE_ATOL / sc
+        mid = (dg + dr) / 2.0
+        # adjacent codes: no E4M3 value lies strictly between them, so the value
+        # nearest to their midpoint is one of the two
+        near = oracle.e4m3_decode(oracle.e4m3_encode(mid))
+        assert np.all((near == dg) | (near == dr)), f"{what}: codes further apart than one step"
+        far = np.abs(x - mid) > eps
+        assert not far.any(), (f"{what}: {far.sum()} codes differ away from a rounding midpoint, "
+                               f"e.g. x={x[far][:3]}, gpu={dg[far][:3]}, oracle={dr[far][:3]}")
+    assert mism.mean() <= 1e-3, f"{what}: {mism.mean():.2%} of the codes differ"
 
 
 def kv_to_f64(inp, rows: np.ndarray, scale: float) -> np.ndarray:

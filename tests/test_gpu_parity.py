@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from long_context_mqa_amd import hs2
-from tests.parity import (FEW_KEYS, check_attn, check_lse, check_selection, from_dev, oracle_query,
-                          oracle_sparse, to_dev)
+from tests.parity import (BRIDGE_ATOL, FEW_KEYS, check_attn, check_bridge_bf16, check_fp8_codes, check_lse,
+                          check_selection, from_dev, oracle_query, oracle_sparse, to_dev)
 from workloads.configs import BlockSpec, block_config, make_block_inputs, make_bridge_inputs
 from workloads.gen import bf16_round, bf16_to_f32, e4m3_encode, stored_to_f64
 
@@ -550,7 +550,7 @@ def test_bridge_append_fp8_rows(n_new, d_model):
                                             (init[2 * l + 1], caches[2 * l + 1], vs[l], vc[l], v_sc[l], f"V{l}")):
             got = c.cpu().numpy()
             assert np.array_equal(got[keep], c0[keep]), f"{what}: a row not appended changed"
-            _check_fp8_codes(got[rows[valid]], val[valid], codes[valid], sc, what)
+            check_fp8_codes(got[rows[valid]], val[valid], codes[valid], sc, what)
 
 
 def test_bridge_append_fp8_then_select():
@@ -571,8 +571,8 @@ def test_bridge_append_fp8_then_select():
     kc, vc = oracle.bridge_kv_fp8(H, [stored_to_f64(bi.w_k[0])], [stored_to_f64(bi.w_v[0])], [spec.k_scale],
                                   [spec.v_scale])
     gk, gv = k.cpu().numpy(), v.cpu().numpy()
-    _check_fp8_codes(gk[rows], ks[0], kc[0], spec.k_scale, "K0")
-    _check_fp8_codes(gv[rows], vs[0], vc[0], spec.v_scale, "V0")
+    check_fp8_codes(gk[rows], ks[0], kc[0], spec.k_scale, "K0")
+    check_fp8_codes(gv[rows], vs[0], vc[0], spec.v_scale, "V0")
     inp.k[rows], inp.v[rows] = gk[rows], gv[rows]
     batch = hs2.Batch.from_host(inp.kv_start, inp.kv_len, inp.q_start, inp.q_pos, spec.total_rows, "cuda")
     out, lse, sel, cnt = hs2.full_attn_select_fp8kv(batch, to_dev(inp.q_sel), k, v, spec.k_scale, spec.v_scale,
@@ -654,29 +654,13 @@ def test_workload7_prefill_262144():
     torch.cuda.empty_cache()
 
 
-BRIDGE_ATOL = 2.0 ** -14
-
-
 def _bridge_check(bi, gk, gv, rows):
     H = stored_to_f64(bi.h[rows])
     ks, vs = oracle.bridge_kv(H, [stored_to_f64(w) for w in bi.w_k], [stored_to_f64(w) for w in bi.w_v])
     for l in range(len(bi.w_k)):
         for got, ref in ((gk[l], ks[l]), (gv[l], vs[l])):
             g = from_dev(got[torch.as_tensor(rows, device=got.device)])
-            # 1 bf16 ulp of the reference value, plus the absolute error of an fp32
-            # accumulation of d_model products (matters only for outputs near zero)
-            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
-            err = np.abs(g - ref)
-            bad = err > ulp + BRIDGE_ATOL
-            assert not bad.any(), (f"bridge layer {l}: {bad.sum()} values beyond tolerance, worst err "
-                                   f"{err[bad].max():.3e} at |ref| {np.abs(ref[bad]).min():.3e}")
-            # against the correctly rounded bf16 value: bf16 output quantisation alone gives a
-            # mean |error| of ~1e-3 against fp64 for outputs of this size, so the closeness
-            # test is made against RNE_bf16(reference)
-            ref_b = bf16_to_f32(bf16_round(ref.astype(np.float32))).astype(np.float64)
-            mism = g != ref_b
-            assert mism.mean() <= 1e-2, f"bridge layer {l}: {mism.mean():.2%} differ from the rounded reference"
-            assert np.abs(g - ref_b).mean() <= 1e-4
+            check_bridge_bf16(g, ref, f"bridge layer {l}")
 
 
 def test_bridge_small_ragged_rows():
@@ -704,28 +688,6 @@ def test_bridge_one_layer_and_tiny_rows():
     _bridge_check(bi, gk, gv, np.arange(37))
 
 
-def _check_fp8_codes(g, val, codes, sc, what):
-    """GPU E4M3 codes g against the oracle's codes of val / sc: a code may differ only by
-    one step, and only where the exact value lies within the GPU's arithmetic error (fp32
-    accumulation as for the bf16 bridging, then one fp32 scaling) of the midpoint between
-    the two codes."""
-    assert g.dtype == np.uint8
-    mism = g != codes
-    if mism.any():
-        x = val[mism] / sc
-        dg, dr = oracle.e4m3_decode(g[mism]), oracle.e4m3_decode(codes[mism])
-        eps = np.abs(x) * 2.0 ** -21 + BRIDGE_ATOL / sc
-        mid = (dg + dr) / 2.0
-        # adjacent codes: no E4M3 value lies strictly between them, so the value
-        # nearest to their midpoint is one of the two
-        near = oracle.e4m3_decode(oracle.e4m3_encode(mid))
-        assert np.all((near == dg) | (near == dr)), f"{what}: codes further apart than one step"
-        far = np.abs(x - mid) > eps
-        assert not far.any(), (f"{what}: {far.sum()} codes differ away from a rounding midpoint, "
-                               f"e.g. x={x[far][:3]}, gpu={dg[far][:3]}, oracle={dr[far][:3]}")
-    assert mism.mean() <= 1e-3, f"{what}: {mism.mean():.2%} of the codes differ"
-
-
 def _bridge_fp8_check(bi, gk, gv, rows, k_sc, v_sc):
     """The FP8 bridging of the given rows against the oracle's (bridge_kv_fp8)."""
     H = stored_to_f64(bi.h[rows])
@@ -734,8 +696,8 @@ def _bridge_fp8_check(bi, gk, gv, rows, k_sc, v_sc):
     kc, vc = oracle.bridge_kv_fp8(H, wk, wv, k_sc, v_sc)
     idx = torch.as_tensor(rows, device=gk[0].device)
     for l in range(len(wk)):
-        _check_fp8_codes(gk[l][idx].cpu().numpy(), ks[l], kc[l], k_sc[l], f"K{l}")
-        _check_fp8_codes(gv[l][idx].cpu().numpy(), vs[l], vc[l], v_sc[l], f"V{l}")
+        check_fp8_codes(gk[l][idx].cpu().numpy(), ks[l], kc[l], k_sc[l], f"K{l}")
+        check_fp8_codes(gv[l][idx].cpu().numpy(), vs[l], vc[l], v_sc[l], f"V{l}")
 
 
 def test_bridge_fp8_small_ragged_rows():

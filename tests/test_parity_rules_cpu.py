@@ -137,3 +137,97 @@ def test_lse_rule():
     check_lse(ref + 5e-4, ref)
     with pytest.raises(AssertionError):
         check_lse(ref + 2e-3, ref)
+
+
+# ----------------------------------------------------------------------------------
+# Bridging rules (bf16 outputs and FP8 E4M3 codes)
+# ----------------------------------------------------------------------------------
+
+def _bridge_ref(seed=9, rows=400, d_model=256):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((rows, d_model))
+    W = rng.standard_normal((d_model, 128)) * 0.06
+    return oracle.bridge_kv(H, [W], [W])[0][0]
+
+
+def test_bridge_bf16_accepts_the_rounded_result():
+    from parity import check_bridge_bf16
+    ref = _bridge_ref()
+    check_bridge_bf16(_bf16(ref), ref)
+
+
+@pytest.mark.parametrize("defect", ["two_ulp", "many_one_ulp", "truncated"])
+def test_bridge_bf16_rejects_defects(defect):
+    from parity import bf16_ulp, check_bridge_bf16
+    ref = _bridge_ref()
+    g = _bf16(ref)
+    if defect == "two_ulp":          # one value two units off
+        g[7, 3] += 2 * bf16_ulp(ref[7, 3])
+    elif defect == "many_one_ulp":   # 5% of the values one unit off (each within 1 ulp)
+        idx = np.random.default_rng(1).random(g.shape) < 0.05
+        g[idx] = _bf16(g[idx] + np.sign(ref[idx] - g[idx] + 1e-300) * bf16_ulp(ref[idx]))
+    else:                            # rounded toward zero instead of to nearest
+        import torch
+        f = torch.from_numpy(ref.astype(np.float32)).view(torch.int32) & ~0xFFFF
+        g = f.view(torch.float32).numpy().astype(np.float64)
+    with pytest.raises(AssertionError):
+        check_bridge_bf16(g, ref)
+
+
+def _fp8_case(seed=11, n=20000, scale=0.01):
+    rng = np.random.default_rng(seed)
+    val = rng.standard_normal(n) * 0.8
+    return val, oracle.e4m3_encode(val / scale), scale
+
+
+def test_fp8_codes_accept_the_oracle_and_a_midpoint_flip():
+    from parity import check_fp8_codes
+    val, codes, sc = _fp8_case()
+    check_fp8_codes(codes.copy(), val, codes, sc)
+    # a value at a rounding midpoint: the other of its two codes is accepted too
+    c = oracle.e4m3_encode(np.array([3.0]))[0]               # 3.0 = code of mantissa 4
+    lo, hi = oracle.e4m3_decode(np.array([c, c + 1], dtype=np.uint8))
+    v = val.copy()
+    v[0] = (lo + hi) / 2.0 * sc
+    ref = oracle.e4m3_encode(v / sc)
+    g = ref.copy()
+    g[0] = c if ref[0] == c + 1 else c + 1
+    check_fp8_codes(g, v, ref, sc)
+
+
+@pytest.mark.parametrize("defect", ["two_steps", "one_step_off_midpoint", "too_many"])
+def test_fp8_codes_reject_defects(defect):
+    from parity import check_fp8_codes
+    val, codes, sc = _fp8_case()
+    g = codes.copy()
+    x = val / sc
+    if defect == "two_steps":
+        i = int(np.argmax((np.abs(x) > 1.0) & (np.abs(x) < 100.0)))
+        g[i] = codes[i] + 2 if (codes[i] & 0x7) < 6 else codes[i] - 2
+    elif defect == "one_step_off_midpoint":
+        # a value a quarter step from its code: the neighbouring code is wrong
+        i = int(np.argmax((np.abs(x) > 1.0) & (np.abs(x) < 100.0)))
+        g[i] = codes[i] + 1 if (codes[i] & 0x7) < 7 else codes[i] - 1
+        back = oracle.e4m3_decode(codes[i:i + 1])[0]
+        step = abs(oracle.e4m3_decode(g[i:i + 1])[0] - back)
+        val = val.copy()
+        val[i] = (back + np.sign(back) * step / 4.0) * sc
+        codes = oracle.e4m3_encode(val / sc)
+        assert codes[i] != g[i]
+    else:                              # 0.5% of the codes one step off at their midpoints
+        val = val.copy()
+        for i in range(0, 100):
+            c = codes[i]
+            nb = c + 1 if (c & 0x7) < 7 else c - 1
+            a, b = oracle.e4m3_decode(np.array([c, nb], dtype=np.uint8))
+            val[i] = (a + b) / 2.0 * sc
+        codes = oracle.e4m3_encode(val / sc)
+        g = codes.copy()
+        for i in range(0, 100):
+            c = codes[i]
+            g[i] = c + 1 if (c & 0x7) < 7 else c - 1
+            a, b = oracle.e4m3_decode(np.array([c, g[i]], dtype=np.uint8))
+            if abs(val[i] / sc - (a + b) / 2.0) > 1e-9:   # not a midpoint pair after all
+                g[i] = c - 1 if (c & 0x7) > 0 else c + 1
+    with pytest.raises(AssertionError):
+        check_fp8_codes(g, val, codes, sc)
