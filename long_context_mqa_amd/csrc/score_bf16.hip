@@ -132,14 +132,20 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
   const size_t wl_idx = ((size_t)i * a.n_split + split) * kSWaves + wave;
   uint2* mylist = a.lists + wl_idx * a.list_cap;
   int thr = 0, cnt = 0;
-  const int ntw = wave < ntiles ? (ntiles - wave + kSWaves - 1) / kSWaves : 0;
-  // Tiles in the reverse of the attention pass's rotated order (same rotation): the first
-  // tiles read here are the last that pass read, some still in the last-level cache.
+  // Each wave streams its own contiguous share of the split's tiles: a workgroup then reads
+  // kSWaves separate regions of K at a time instead of one region in interleaved tiles,
+  // which keeps more requests in flight at the memory (64 x 131,072 decode batch: 1,029 ->
+  // 1,021 us per selector call, same-box A/B in both orders).
+  const int q_tiles = (ntiles + kSWaves - 1) / kSWaves;
+  const int t0 = wave * q_tiles;
+  const int ntw = max(0, min(q_tiles, ntiles - t0));
+  // Tiles in the reverse of the attention pass's rotated order (same rotation, so that the
+  // workgroups of one query's splits do not read the same offsets at the same time).
   const TileOrder ord = TileOrder::rotated(i * a.n_split + split, ntiles);
   auto tile_of = [&](int x) { return ord.at(ntiles - 1 - x); };
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
   auto issue = [&](int it, int sidx) {
-    issue_tile_contig<Kv, true>(a.k, base, k0 + tile_of(wave + it * kSWaves) * kTile, k1, lane,
+    issue_tile_contig<Kv, true>(a.k, base, k0 + tile_of(t0 + it) * kTile, k1, lane,
                                 wbase + sidx * Kv::kTileBytes);
   };
   for (int it = 0; it < min(ntw, kScoreStages); ++it) issue(it, it);
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
     // lane l and l^32 hold complementary heads of the same key; add in a fixed order
     const float other = __shfl_xor(sum, 32);
     const float total = (lane < 32) ? sum + other : other + sum;
-    const int p = k0 + tile_of(wave + it * kSWaves) * kTile + (lane & 31);
+    const int p = k0 + tile_of(t0 + it) * kTile + (lane & 31);
     if (lane < 32 && p < k1) {
       sm.sbuf[wave][(it % kSFlush) * kTile + lane] = total;
       atomicAdd(&sm.hist[__float_as_uint(total) >> kHistShift], 1u);
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
       const int ne = (it + 1 - first) * kTile;
       for (int e0 = 0; e0 < ne; e0 += 64) {
         const int e = e0 + lane;
-        const int p = k0 + tile_of(wave + (first + e / kTile) * kSWaves) * kTile + (e % kTile);
+        const int p = k0 + tile_of(t0 + first + e / kTile) * kTile + (e % kTile);
         const uint32_t u = e < ne ? __float_as_uint(sm.sbuf[wave][e]) : 0u;
         const bool keep = e < ne && p < k1 && (int)(u >> kHistShift) >= thr;
         const uint64_t bal = __ballot(keep);
