@@ -42,20 +42,22 @@ struct AttnSmem {
 };
 
 // The tiles of the workgroup's key range that one wave streams: tile x(it) = t0 + it * stride
-// of the rotated order, it < n. bf16 K/V (four waves): each wave a contiguous share, so that a
-// workgroup reads eight separate regions (K and V of four shares) at a time; on the 64 x 131,072
-// decode batch this took 6-11 us off a selector call (same-box A/B, both orders). FP8 K/V (eight
-// waves, two per SIMD): interleaved tiles, which measured 8-16 us faster there than shares.
+// of the rotated order, it < n. The split is cut into kW / g contiguous chunks, each streamed
+// by g waves in interleaved tiles, so that a workgroup reads 2 kW / g separate regions of K
+// and V at a time. bf16 K/V (four waves): g = 2, four regions; on the 64 x 131,072 decode
+// batch 7-9 us per selector call faster than g = 1 (eight regions), which was itself 6-11 us
+// faster than g = 4 (two regions; same-box A/Bs, both orders). FP8 K/V (eight waves, bound by
+// the per-tile conversion chain): g = 8; groups of 4 or 2 measured within noise of it.
 struct WaveTiles {
   int t0, stride, n;
   template <typename Kv, int kW>
   __device__ static WaveTiles of(int wave, int ntiles) {
-    if constexpr (!Kv::kFp8) {
-      const int q = (ntiles + kW - 1) / kW;
-      return WaveTiles{wave * q, 1, max(0, min(q, ntiles - wave * q))};
-    } else {
-      return WaveTiles{wave, kW, wave < ntiles ? (ntiles - wave + kW - 1) / kW : 0};
-    }
+    constexpr int g = Kv::kFp8 ? kW : 2;  // waves per chunk
+    if constexpr (g == kW) return WaveTiles{wave, kW, wave < ntiles ? (ntiles - wave + kW - 1) / kW : 0};
+    const int c = wave / g, r = wave % g;
+    const int qc = (ntiles + kW / g - 1) / (kW / g);  // tiles per chunk
+    const int len = max(0, min(qc, ntiles - c * qc));
+    return WaveTiles{c * qc + r, g, r < len ? (len - r + g - 1) / g : 0};
   }
   __device__ int at(int it) const { return t0 + it * stride; }
 };
