@@ -139,8 +139,9 @@ __global__ __launch_bounds__(64 * ScoreCfg<Kv>::kSWaves) void score_bf16_kernel(
   const int q_tiles = (ntiles + kSWaves - 1) / kSWaves;
   const int t0 = wave * q_tiles;
   const int ntw = max(0, min(q_tiles, ntiles - t0));
-  // Tiles in the reverse of the attention pass's rotated order (same rotation, so that the
-  // workgroups of one query's splits do not read the same offsets at the same time).
+  // Tiles in the reverse of the attention pass's rotated order (the same per-workgroup
+  // rotation, so that workgroups streaming equal splits do not read the same offsets at
+  // the same time).
   const TileOrder ord = TileOrder::rotated(i * a.n_split + split, ntiles);
   auto tile_of = [&](int x) { return ord.at(ntiles - 1 - x); };
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)sm.stage[wave]);
