@@ -149,8 +149,8 @@ def to_dev(a, device="cuda"):
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a "
-              f"single MI355X; multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on a "
+              f"single MI355X; how the path would shard over several GPUs is described, not built)", file=sys.stderr)
         return 2
     import numpy as np
     import torch
